@@ -1,0 +1,54 @@
+"""Turn generated torch tensors into the oracle's numpy inputs (exact values)."""
+import numpy as np
+import torch
+
+from oracle import moe_oracle as O
+
+
+def exact(t: torch.Tensor) -> np.ndarray:
+    """bf16 / fp32 tensor -> float64 numpy array of the same values."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def codes(t: torch.Tensor) -> np.ndarray:
+    """float8_e4m3fn tensor -> uint8 codes."""
+    return t.detach().to("cpu").contiguous().view(torch.uint8).numpy()
+
+
+def expert_fn(tens, device_to_host=True):
+    """(expert(e), shared()) accessors returning fp64 [out, in] matrices for the oracle."""
+    fp8 = tens.shape.dtype == "fp8"
+
+    def mat(w, s):
+        if fp8:
+            return O.dequant_128x128(codes(w), s.detach().cpu().numpy())
+        return exact(w)
+
+    def expert(e):
+        if fp8:
+            return (mat(tens.w1[e], tens.s1[e]), mat(tens.w3[e], tens.s3[e]), mat(tens.w2[e], tens.s2[e]))
+        return exact(tens.w1[e]), exact(tens.w3[e]), exact(tens.w2[e])
+
+    def shared():
+        if fp8:
+            return mat(tens.ws1, tens.ss1), mat(tens.ws3, tens.ss3), mat(tens.ws2, tens.ss2)
+        return exact(tens.ws1), exact(tens.ws3), exact(tens.ws2)
+
+    return expert, shared
+
+
+def act_out(shape):
+    """(activation storage dtype, output dtype) of a workload."""
+    return {"f32": ("f32", "f32"), "bf16": ("bf16", "bf16"), "fp8": ("fp8", "bf16")}[shape.dtype]
+
+
+def bias_np(tens):
+    return None if tens.bias is None else tens.bias.detach().cpu().numpy().astype(np.float32)
+
+
+def oracle_forward(tens, x=None):
+    """Run the oracle block on tens (optionally on a subset of tokens x [n, D] fp64)."""
+    expert, shared = expert_fn(tens)
+    act, out = act_out(tens.shape)
+    xx = exact(tens.x) if x is None else x
+    return O.moe_forward(tens.shape, xx, exact(tens.w_gate), bias_np(tens), expert, shared, act, out)
