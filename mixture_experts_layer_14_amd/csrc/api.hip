@@ -1,0 +1,355 @@
+// The C ABI of libmoe (declared and documented in include/moe.h): argument checks,
+// workspace planning, and the stream-ordered launch sequence of the block.
+#include <string.h>
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  moe_ws_layout pub;
+  size_t meta, blk, tiles_s, tiles_w, zpart;
+  int nsplit;
+};
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_config(const moe_config* c, int64_t T, moe::Dims* d) {
+  if (!c) return fail(MOE_ERR_ARG, "cfg is NULL");
+  if (T < 0) return fail(MOE_ERR_ARG, "T < 0");
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16 && c->dtype != MOE_FP8)
+    return fail(MOE_ERR_CONFIG, "unknown dtype");
+  if (c->dim <= 0 || c->n_experts <= 0 || c->n_groups <= 0 || c->topk_groups <= 0 || c->topk <= 0 ||
+      c->inter <= 0 || c->n_shared <= 0)
+    return fail(MOE_ERR_CONFIG, "every size in cfg must be positive");
+  if (c->n_experts % c->n_groups) return fail(MOE_ERR_CONFIG, "n_experts must be a multiple of n_groups");
+  if (c->topk_groups > c->n_groups) return fail(MOE_ERR_CONFIG, "topk_groups > n_groups");
+  if ((int64_t)c->topk > (int64_t)c->topk_groups * (c->n_experts / c->n_groups))
+    return fail(MOE_ERR_CONFIG, "topk exceeds the experts of the kept groups");
+  if (!(c->route_scale == c->route_scale)) return fail(MOE_ERR_CONFIG, "route_scale is NaN");
+  if (c->n_experts > 1024 || c->n_groups > 64 || c->topk > 16)
+    return fail(MOE_ERR_UNSUPPORTED, "kernels handle n_experts <= 1024, n_groups <= 64, topk <= 16");
+  const int64_t S = (int64_t)c->n_shared * c->inter;
+  if (c->dtype == MOE_BF16 && (c->dim % 128 || c->inter % 32 || S % 32))
+    return fail(MOE_ERR_UNSUPPORTED, "bf16 needs dim % 128 == 0 and inter % 32 == 0");
+  if (c->dtype == MOE_FP8 && (c->dim % 128 || c->inter % 128))
+    return fail(MOE_ERR_UNSUPPORTED, "fp8 needs dim and inter multiples of 128");
+  if ((int64_t)T * c->topk >= (int64_t)1 << 31 || T * (int64_t)c->dim >= (int64_t)1 << 40)
+    return fail(MOE_ERR_UNSUPPORTED, "too many tokens");
+  d->T = T;
+  d->R = T * c->topk;
+  d->D = c->dim;
+  d->E = c->n_experts;
+  d->G = c->n_groups;
+  d->Gk = c->topk_groups;
+  d->K = c->topk;
+  d->I = c->inter;
+  d->S = (int)S;
+  d->dtype = c->dtype;
+  return MOE_OK;
+}
+
+Layout plan(const moe::Dims& d) {
+  Layout L;
+  memset(&L, 0, sizeof(L));
+  const size_t act = d.dtype == MOE_F32 ? 4 : d.dtype == MOE_BF16 ? 2 : 1;
+  const size_t outb = d.dtype == MOE_F32 ? 4 : 2;
+  const bool fp8 = d.dtype == MOE_FP8;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.pub.idx = take(d.R * 4);
+  L.pub.w = take(d.R * 4);
+  L.pub.counts = take((size_t)d.E * 4);
+  L.pub.offsets = take(((size_t)d.E + 1) * 4);
+  L.pub.row_token = take(d.R * 4);
+  L.pub.row_of = take(d.R * 4);
+  L.meta = take(moe::kMetaInts * 4);
+  L.blk = take((size_t)std::max(1, moe::dispatch_blocks(d.T)) * d.E * 4);
+  L.tiles_s = take((size_t)moe::max_tiles(d, moe::kSkinnyBM) * sizeof(Tile));
+  L.tiles_w = take((size_t)moe::max_tiles(d, moe::kWideBM) * sizeof(Tile));
+  L.nsplit = moe::router_splits(d);
+  L.zpart = take((size_t)L.nsplit * d.T * d.E * 8);
+  L.pub.xq = take(fp8 ? (size_t)d.T * d.D : 0);
+  L.pub.x_scale = take(fp8 ? (size_t)d.T * (d.D / 128) * 4 : 0);
+  L.pub.h_routed = take((size_t)d.R * d.I * act);
+  L.pub.h_shared = take((size_t)d.T * d.S * act);
+  L.pub.h_scale = take(fp8 ? (size_t)d.R * (d.I / 128) * 4 : 0);
+  L.pub.h_shared_scale = take(fp8 ? (size_t)d.T * (d.S / 128) * 4 : 0);
+  L.pub.o_routed = take((size_t)d.R * d.D * outb);
+  L.pub.o_shared = take((size_t)d.T * d.D * outb);
+  L.pub.total = o;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+moe_status check_ws(const Layout& L, const void* ws, size_t ws_bytes) {
+  if (ws_bytes < L.pub.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace of " + std::to_string(ws_bytes) + " bytes, need " +
+                                       std::to_string(L.pub.total));
+  if (!ws && L.pub.total) return fail(MOE_ERR_ARG, "ws is NULL");
+  if (!aligned16(ws)) return fail(MOE_ERR_ARG, "ws is not 16-byte aligned");
+  return MOE_OK;
+}
+
+// ---- measurement spans (moe_timing_enable / moe_timing_report)
+struct SpanRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<hipEvent_t> g_pool;
+std::vector<SpanRec> g_spans;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void drop_spans() {
+  for (auto& r : g_spans) {
+    if (r.a) g_pool.push_back(r.a);
+    if (r.b) g_pool.push_back(r.b);
+  }
+  g_spans.clear();
+}
+
+}  // namespace
+
+namespace moe {
+void span_begin(const char* name, hipStream_t s) {
+  if (!g_timing) return;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  SpanRec r{name, take_event(), nullptr};
+  if (r.a) (void)hipEventRecord(r.a, s);
+  g_spans.push_back(r);
+}
+void span_end(hipStream_t s) {
+  if (!g_timing) return;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (g_spans.empty() || g_spans.back().b) return;
+  hipEvent_t e = take_event();
+  if (e) (void)hipEventRecord(e, s);
+  g_spans.back().b = e;
+}
+}  // namespace moe
+
+extern "C" {
+
+moe_status moe_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  drop_spans();
+  if (on) {
+    // make sure events can be created before claiming success
+    hipEvent_t e = take_event();
+    if (!e) return fail(MOE_ERR_HIP, "hipEventCreate failed");
+    g_pool.push_back(e);
+  }
+  g_timing = on != 0;
+  return MOE_OK;
+}
+
+int moe_timing_report(char* buf, size_t bytes) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  std::map<std::string, std::pair<long, double>> acc;
+  std::vector<std::string> order;
+  for (auto& r : g_spans) {
+    if (!r.a || !r.b) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) {
+      drop_spans();
+      return fail(MOE_ERR_HIP, "hipEventSynchronize failed");
+    }
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, r.a, r.b);
+    auto it = acc.find(r.name);
+    if (it == acc.end()) {
+      order.push_back(r.name);
+      acc[r.name] = {1, ms};
+    } else {
+      it->second.first += 1;
+      it->second.second += ms;
+    }
+  }
+  drop_spans();
+  std::string out;
+  for (auto& n : order) {
+    char line[256];
+    snprintf(line, sizeof(line), "%s %ld %.6f\n", n.c_str(), acc[n].first, acc[n].second);
+    out += line;
+  }
+  if (buf && bytes) {
+    size_t n = std::min(bytes - 1, out.size());
+    memcpy(buf, out.data(), n);
+    buf[n] = 0;
+  }
+  return (int)order.size();
+}
+
+moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes) {
+  moe::Dims d;
+  if (!bytes) return fail(MOE_ERR_ARG, "bytes is NULL");
+  moe_status st = check_config(cfg, T, &d);
+  if (st != MOE_OK) return st;
+  *bytes = plan(d).pub.total;
+  return MOE_OK;
+}
+
+moe_status moe_workspace_layout(const moe_config* cfg, int64_t T, moe_ws_layout* layout) {
+  moe::Dims d;
+  if (!layout) return fail(MOE_ERR_ARG, "layout is NULL");
+  moe_status st = check_config(cfg, T, &d);
+  if (st != MOE_OK) return st;
+  *layout = plan(d).pub;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_config* cfg, const void* w_gate, const float* bias, const void* x, int64_t T,
+                     int32_t* idx, float* w, void* ws, size_t ws_bytes, void* stream) {
+  moe::Dims d;
+  moe_status st = check_config(cfg, T, &d);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!w_gate || !x || !idx || !w) return fail(MOE_ERR_ARG, "NULL tensor argument");
+  if (!aligned16(w_gate) || !aligned16(x) || !aligned16(bias) || !aligned16(idx) || !aligned16(w))
+    return fail(MOE_ERR_ARG, "device pointers must be 16-byte aligned");
+  if (bias && d.G > 1 && d.E / d.G < 2) return fail(MOE_ERR_CONFIG, "top-2 group score needs 2 experts per group");
+  Layout L = plan(d);
+  if ((st = check_ws(L, ws, ws_bytes)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  double* zpart = at<double>(ws, L.zpart);
+  if ((st = hip_status(moe::launch_router_logits(d, x, w_gate, zpart, L.nsplit, s), "router logits")) != MOE_OK)
+    return st;
+  return hip_status(moe::launch_router_select(d, zpart, L.nsplit, bias, cfg->route_scale, idx, w, s),
+                    "router select");
+}
+
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* idx, int64_t T, int32_t* counts, int32_t* offsets,
+                        int32_t* row_token, int32_t* row_of, void* ws, size_t ws_bytes, void* stream) {
+  moe::Dims d;
+  moe_status st = check_config(cfg, T, &d);
+  if (st != MOE_OK) return st;
+  if (!counts || !offsets || (T > 0 && (!idx || !row_token || !row_of)))
+    return fail(MOE_ERR_ARG, "NULL tensor argument");
+  Layout L = plan(d);
+  if ((st = check_ws(L, ws, ws_bytes)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(moe::launch_dispatch(d, idx, at<int32_t>(ws, L.blk), counts, offsets, row_token, row_of,
+                                         at<int32_t>(ws, L.meta), at<Tile>(ws, L.tiles_s),
+                                         at<Tile>(ws, L.tiles_w), s),
+                    "dispatch");
+}
+
+moe_status moe_forward(const moe_config* cfg, const moe_weights* wts, const void* x, int64_t T, void* out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  moe::Dims d;
+  moe_status st = check_config(cfg, T, &d);
+  if (st != MOE_OK) return st;
+  if (!wts) return fail(MOE_ERR_ARG, "wts is NULL");
+  if (T == 0) return MOE_OK;
+  if (!x || !out || !wts->w_gate || !wts->w1 || !wts->w3 || !wts->w2 || !wts->ws1 || !wts->ws3 || !wts->ws2)
+    return fail(MOE_ERR_ARG, "NULL tensor argument");
+  const bool fp8 = d.dtype == MOE_FP8;
+  if (fp8 && (!wts->s1 || !wts->s3 || !wts->s2 || !wts->ss1 || !wts->ss3 || !wts->ss2))
+    return fail(MOE_ERR_ARG, "fp8 weights need their block scales");
+  const void* ptrs[] = {x, out, wts->w_gate, wts->bias, wts->w1, wts->w3, wts->w2, wts->ws1, wts->ws3, wts->ws2};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(MOE_ERR_ARG, "device pointers must be 16-byte aligned");
+  if (wts->bias && d.G > 1 && d.E / d.G < 2)
+    return fail(MOE_ERR_CONFIG, "top-2 group score needs 2 experts per group");
+  Layout L = plan(d);
+  if ((st = check_ws(L, ws, ws_bytes)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  int32_t* idx = at<int32_t>(ws, L.pub.idx);
+  float* w = at<float>(ws, L.pub.w);
+  int32_t* offsets = at<int32_t>(ws, L.pub.offsets);
+  int32_t* row_token = at<int32_t>(ws, L.pub.row_token);
+  int32_t* row_of = at<int32_t>(ws, L.pub.row_of);
+  int32_t* meta = at<int32_t>(ws, L.meta);
+  double* zpart = at<double>(ws, L.zpart);
+
+  if (fp8 && (st = hip_status(moe::launch_act_quant(d, static_cast<const bf16_t*>(x), at<uint8_t>(ws, L.pub.xq),
+                                                    at<float>(ws, L.pub.x_scale), s),
+                              "activation quantisation")) != MOE_OK)
+    return st;
+  if ((st = hip_status(moe::launch_router_logits(d, x, wts->w_gate, zpart, L.nsplit, s), "router logits")) != MOE_OK)
+    return st;
+  if ((st = hip_status(moe::launch_router_select(d, zpart, L.nsplit, wts->bias, cfg->route_scale, idx, w, s),
+                       "router select")) != MOE_OK)
+    return st;
+  if ((st = hip_status(moe::launch_dispatch(d, idx, at<int32_t>(ws, L.blk), at<int32_t>(ws, L.pub.counts), offsets,
+                                            row_token, row_of, meta, at<Tile>(ws, L.tiles_s),
+                                            at<Tile>(ws, L.tiles_w), s),
+                       "dispatch")) != MOE_OK)
+    return st;
+  moe::ExpertPtrs ep{wts->w1, wts->w3, wts->w2, wts->ws1, wts->ws3, wts->ws2,
+                     wts->s1, wts->s3, wts->s2, wts->ss1, wts->ss3, wts->ss2};
+  moe::Act act;
+  act.x = fp8 ? static_cast<const void*>(at<uint8_t>(ws, L.pub.xq)) : x;
+  act.x_scale = fp8 ? at<float>(ws, L.pub.x_scale) : nullptr;
+  act.row_token = row_token;
+  act.offsets = offsets;
+  act.meta = meta;
+  act.tiles_skinny = at<Tile>(ws, L.tiles_s);
+  act.tiles_wide = at<Tile>(ws, L.tiles_w);
+  act.h_routed = at<void>(ws, L.pub.h_routed);
+  act.h_shared = at<void>(ws, L.pub.h_shared);
+  act.h_scale = fp8 ? at<float>(ws, L.pub.h_scale) : nullptr;
+  act.h_shared_scale = fp8 ? at<float>(ws, L.pub.h_shared_scale) : nullptr;
+  act.o_routed = at<void>(ws, L.pub.o_routed);
+  act.o_shared = at<void>(ws, L.pub.o_shared);
+  if ((st = hip_status(moe::launch_experts(d, ep, act, s), "experts")) != MOE_OK) return st;
+  return hip_status(moe::launch_combine(d, idx, w, row_of, act.o_routed, act.o_shared, out, s), "combine");
+}
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument";
+    case MOE_ERR_CONFIG: return "invalid configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Host-side launchers of the libmoe kernels (internal; the public ABI is include/moe.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace moe {
+
+// Measurement spans: when timing is enabled (moe_timing_enable), each kernel launch is
+// bracketed by HIP events on its stream; otherwise these do nothing.
+void span_begin(const char* name, hipStream_t s);
+void span_end(hipStream_t s);
+struct Span {
+  hipStream_t s;
+  Span(const char* name, hipStream_t st) : s(st) { span_begin(name, st); }
+  ~Span() { span_end(s); }
+};
+// Launch `kernel` on stream `s` (a variable in scope) inside a measurement span.
+#define MOE_LAUNCH(kernel, ...)                         \
+  do {                                                  \
+    ::moe::Span sp_(#kernel, s);                        \
+    hipLaunchKernelGGL(kernel, __VA_ARGS__);            \
+  } while (0)
+
+// Rows per M-tile of the tile lists the dispatch writes.
+constexpr int kSkinnyBM = 16;
+constexpr int kWideBM = 128;
+constexpr int kDispatchTB = 256;  // tokens per dispatch block
+
+// meta[] written by dispatch_scan (int32):
+//   [0] routed tiles (BM 16)   [1] all tiles (BM 16)
+//   [2] routed tiles (BM 128)  [3] all tiles (BM 128)
+//   [4] experts with tokens
+constexpr int kMetaInts = 8;
+
+struct Dims {
+  int64_t T, R;            // tokens, routed rows (T * K)
+  int D, E, G, Gk, K, I, S;
+  int dtype;               // moe_dtype
+};
+
+// ---- router
+int router_splits(const Dims& d);
+hipError_t launch_router_logits(const Dims& d, const void* x, const void* w_gate, double* zpart, int nsplit,
+                                hipStream_t s);
+hipError_t launch_router_select(const Dims& d, const double* zpart, int nsplit, const float* bias,
+                                float route_scale, int32_t* idx, float* w, hipStream_t s);
+
+// ---- dispatch
+int dispatch_blocks(int64_t T);
+hipError_t launch_dispatch(const Dims& d, const int32_t* idx, int32_t* blk, int32_t* counts, int32_t* offsets,
+                           int32_t* row_token, int32_t* row_of, int32_t* meta, Tile* tiles_skinny,
+                           Tile* tiles_wide, hipStream_t s);
+int64_t max_tiles(const Dims& d, int bm);
+
+// ---- fp8 activation quantisation (x -> e4m3 + per 1x128 scales)
+hipError_t launch_act_quant(const Dims& d, const bf16_t* x, uint8_t* xq, float* sx, hipStream_t s);
+
+// ---- expert GEMMs
+struct ExpertPtrs {
+  const void *w1, *w3, *w2, *ws1, *ws3, *ws2;
+  const float *s1, *s3, *s2, *ss1, *ss3, *ss2;
+};
+struct Act {
+  const void* x;            // [T, D] x (f32 / bf16) or xq (e4m3)
+  const float* x_scale;     // fp8: [T, D/128]
+  const int32_t* row_token; // [R]
+  const int32_t* offsets;   // [E + 1]
+  const int32_t* meta;
+  const Tile* tiles_skinny;
+  const Tile* tiles_wide;
+  void* h_routed;           // [R, I]
+  void* h_shared;           // [T, S]
+  float* h_scale;           // fp8: [R, I/128]
+  float* h_shared_scale;    // fp8: [T, S/128]
+  void* o_routed;           // [R, D]
+  void* o_shared;           // [T, D]
+};
+hipError_t launch_experts(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
+
+// ---- combine
+hipError_t launch_combine(const Dims& d, const int32_t* idx, const float* w, const int32_t* row_of,
+                          const void* o_routed, const void* o_shared, void* out, hipStream_t s);
+
+}  // namespace moe

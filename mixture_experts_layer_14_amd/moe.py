@@ -1,0 +1,177 @@
+"""ctypes binding of libmoe (include/moe.h). Argument marshalling only: every step of the
+block runs in the library's HIP kernels. torch tensors supply device memory and streams.
+
+Loading fails loudly when libmoe.so has not been built; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from .inputs import MoeShape, MoeTensors
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+_lib = None
+
+MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
+_DTYPE = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8}
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_CONFIG", -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP",
+          -5: "MOE_ERR_UNSUPPORTED"}
+
+#: Every function include/moe.h declares.
+EXPORTS = ["moe_workspace_size", "moe_route", "moe_dispatch", "moe_forward", "moe_workspace_layout",
+           "moe_status_str", "moe_last_error", "moe_timing_enable", "moe_timing_report"]
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [("dim", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("topk_groups", ctypes.c_int32), ("topk", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_shared", ctypes.c_int32), ("route_scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ["w_gate", "bias", "w1", "w3", "w2", "ws1", "ws3", "ws2", "s1", "s3", "s2", "ss1", "ss3", "ss2"]]
+
+
+class MoeWsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ["idx", "w", "counts", "offsets", "row_token", "row_of", "h_routed", "h_shared", "h_scale",
+                 "h_shared_scale", "o_routed", "o_shared", "xq", "x_scale", "total"]]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with python -m mixture_experts_layer_14_amd.build")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        L.moe_workspace_size.argtypes = [ctypes.POINTER(MoeConfig), i64, ctypes.POINTER(sz)]
+        L.moe_workspace_layout.argtypes = [ctypes.POINTER(MoeConfig), i64, ctypes.POINTER(MoeWsLayout)]
+        L.moe_route.argtypes = [ctypes.POINTER(MoeConfig), vp, vp, vp, i64, vp, vp, vp, sz, vp]
+        L.moe_dispatch.argtypes = [ctypes.POINTER(MoeConfig), vp, i64, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_forward.argtypes = [ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeWeights), vp, i64, vp, vp, sz, vp]
+        for f in ["moe_workspace_size", "moe_workspace_layout", "moe_route", "moe_dispatch", "moe_forward"]:
+            getattr(L, f).restype = ctypes.c_int
+        L.moe_status_str.argtypes = [ctypes.c_int]
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_timing_enable.argtypes = [ctypes.c_int]
+        L.moe_timing_enable.restype = ctypes.c_int
+        L.moe_timing_report.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
+        L.moe_timing_report.restype = ctypes.c_int
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MoeError(status, where, lib().moe_last_error().decode())
+
+
+def config(shape: MoeShape) -> MoeConfig:
+    return MoeConfig(shape.dim, shape.n_experts, shape.n_groups, shape.topk_groups, shape.topk, shape.inter,
+                     shape.n_shared, shape.route_scale, _DTYPE[shape.dtype])
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> Optional[int]:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def workspace_size(cfg: MoeConfig, tokens: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_workspace_size(ctypes.byref(cfg), tokens, ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def workspace_layout(cfg: MoeConfig, tokens: int) -> MoeWsLayout:
+    lay = MoeWsLayout()
+    _check(lib().moe_workspace_layout(ctypes.byref(cfg), tokens, ctypes.byref(lay)), "moe_workspace_layout")
+    return lay
+
+
+def weights(t: MoeTensors) -> MoeWeights:
+    return MoeWeights(*[_ptr(getattr(t, n)) for n in
+                        ["w_gate", "bias", "w1", "w3", "w2", "ws1", "ws3", "ws2", "s1", "s3", "s2", "ss1", "ss3",
+                         "ss2"]])
+
+
+def route(cfg: MoeConfig, w_gate, bias, x, idx, w, ws, stream=None):
+    _check(lib().moe_route(ctypes.byref(cfg), _ptr(w_gate), _ptr(bias), _ptr(x), x.shape[0], _ptr(idx), _ptr(w),
+                           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_route")
+
+
+def dispatch(cfg: MoeConfig, idx, counts, offsets, row_token, row_of, ws, stream=None):
+    _check(lib().moe_dispatch(ctypes.byref(cfg), _ptr(idx), idx.shape[0], _ptr(counts), _ptr(offsets),
+                              _ptr(row_token), _ptr(row_of), _ptr(ws), ws.numel() * ws.element_size(),
+                              _stream(stream)), "moe_dispatch")
+
+
+def forward(cfg: MoeConfig, wts: MoeWeights, x, out, ws, stream=None, tokens: Optional[int] = None):
+    n = x.shape[0] if tokens is None else tokens
+    _check(lib().moe_forward(ctypes.byref(cfg), ctypes.byref(wts), _ptr(x), n, _ptr(out), _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+def timing_enable(on: bool):
+    _check(lib().moe_timing_enable(1 if on else 0), "moe_timing_enable")
+
+
+def timing_report() -> dict:
+    """{kernel name: (launches, total ms)} since timing was enabled; clears the records."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    n = lib().moe_timing_report(buf, len(buf))
+    if n < 0:
+        _check(n, "moe_timing_report")
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.rsplit(" ", 2)
+        out[name] = (int(cnt), float(ms))
+    return out
+
+
+@dataclass
+class Block:
+    """One MoE block on the GPU: weights, a workspace sized for up to `max_tokens`, and forward()."""
+
+    tensors: MoeTensors
+    max_tokens: int
+
+    def __post_init__(self):
+        self.cfg = config(self.tensors.shape)
+        self.wts = weights(self.tensors)
+        dev = self.tensors.x.device
+        self.ws = torch.empty(workspace_size(self.cfg, self.max_tokens), dtype=torch.uint8, device=dev)
+
+    def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty_like(x)
+        forward(self.cfg, self.wts, x, out, self.ws, stream)
+        return out
+
+    def layout(self, tokens: int) -> MoeWsLayout:
+        return workspace_layout(self.cfg, tokens)
+
+    def ws_view(self, tokens: int, name: str, dtype: torch.dtype, count: int) -> torch.Tensor:
+        """A typed view of an intermediate in the workspace (valid after forward on `tokens`)."""
+        off = getattr(self.layout(tokens), name)
+        nbytes = count * torch.empty((), dtype=dtype).element_size()
+        return self.ws[off:off + nbytes].view(dtype)

@@ -1,0 +1,198 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded synthetic inputs.
+
+Small shapes are checked on every token and span several tiles with ragged tails; the full
+DeepSeek-V3 shapes (decode 16, prefill 4096, skewed 4096, fp8 16384 tokens) are checked on
+routing and dispatch for every token and on the outputs of sampled tokens, in the launch
+configuration the bench times."""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_14_amd import inputs, moe
+from oracle import moe_oracle as O
+from tests.oracle_io import bias_np, exact, oracle_forward
+from tests.parity import dispatch_check, np_i32, out_check, route_check, say, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+S = inputs.MoeShape
+
+SMALL = {
+    "tiny_fp32": inputs.WORKLOADS["tiny_fp32"],
+    "ragged_fp32": S("ragged_fp32", tokens=37, dim=100, n_experts=12, n_groups=3, topk_groups=2, topk=3, inter=40,
+                     n_shared=2, route_scale=1.5, dtype="f32"),
+    "mid_bf16": S("mid_bf16", tokens=300, dim=1024, n_experts=64, n_groups=8, topk_groups=4, topk=8, inter=160,
+                  n_shared=1, route_scale=2.5, dtype="bf16"),
+    "mid_bf16_shared2": S("mid_bf16_shared2", tokens=77, dim=512, n_experts=32, n_groups=4, topk_groups=2, topk=6,
+                          inter=96, n_shared=2, route_scale=2.5, dtype="bf16", hot_bias=0.5),
+    "mid_fp8": S("mid_fp8", tokens=200, dim=1024, n_experts=32, n_groups=4, topk_groups=2, topk=6, inter=256,
+                 n_shared=1, route_scale=2.5, dtype="fp8"),
+    "wide_bf16": S("wide_bf16", tokens=700, dim=768, n_experts=16, n_groups=4, topk_groups=2, topk=4, inter=256,
+                   n_shared=1, route_scale=2.5, dtype="bf16", hot_bias=0.5),
+}
+FULL = ["decode_bf16", "prefill_bf16", "skewed_bf16", "prefill_fp8"]
+
+
+def run_block(tens, tokens=None):
+    t = tens.shape.tokens if tokens is None else tokens
+    blk = moe.Block(tens, max(t, 1))
+    out = blk.forward(tens.x[:t])
+    torch.cuda.synchronize()
+    return blk, out
+
+
+def gpu_route(blk, shape, T):
+    K = shape.topk
+    gidx = np_i32(blk.ws_view(T, "idx", torch.int32, T * K).view(T, K))
+    gw = blk.ws_view(T, "w", torch.float32, T * K).view(T, K).cpu().numpy()
+    return gidx, gw
+
+
+def gpu_dispatch(blk, shape, T):
+    E, R = shape.n_experts, T * shape.topk
+    v = lambda n, c: np_i32(blk.ws_view(T, n, torch.int32, c))  # noqa: E731
+    return v("counts", E), v("offsets", E + 1), v("row_token", R), v("row_of", R)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small_all_tokens(name):
+    shape = SMALL[name]
+    say(f"[forward/small] {name} T={shape.tokens} D={shape.dim} E={shape.n_experts} dtype={shape.dtype}")
+    tens = inputs.generate(shape, seed=0, device=DEV)
+    blk, out = run_block(tens)
+    f = oracle_forward(tens)
+    gidx, gw = gpu_route(blk, shape, shape.tokens)
+    bad, rep = route_check(shape, f.route, gidx, gw)
+    dispatch_check(shape, gidx, *gpu_dispatch(blk, shape, shape.tokens))
+    orep = out_check(shape, to_np(out), f.out, skip=bad)
+    say(f"  route {rep}\n  out {orep}")
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full_shape(name):
+    shape = inputs.WORKLOADS[name]
+    T = shape.tokens
+    say(f"[forward/full] {name} T={T} dtype={shape.dtype}: generating weights")
+    tens = inputs.generate(shape, seed=0, device=DEV)
+    say("  running the block")
+    blk, out = run_block(tens)
+    say("  oracle routing on every token")
+    r = O.route(shape, exact(tens.x), exact(tens.w_gate), bias_np(tens))
+    gidx, gw = gpu_route(blk, shape, T)
+    bad, rep = route_check(shape, r, gidx, gw)
+    say(f"  route {rep}")
+    dispatch_check(shape, gidx, *gpu_dispatch(blk, shape, T))
+    rng = np.random.default_rng(1)
+    n = T if T <= 16 else 10
+    sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n, replace=False)]))[:max(n, 2)]
+    say(f"  oracle forward on {len(sample)} tokens")
+    f = oracle_forward(tens, x=exact(tens.x)[sample])
+    orep = out_check(shape, to_np(out)[sample], f.out, skip=bad[sample])
+    say(f"  out {orep}")
+    if name == "skewed_bf16":
+        hot = np.isin(r.idx, np.arange(0, shape.n_experts, 8)).mean()
+        say(f"  fraction of assignments on the 32 biased experts: {hot:.4f}")
+
+
+@pytest.mark.parametrize("T", [1, 17, 64])
+def test_token_counts_edges(T):
+    shape = SMALL["mid_bf16"].with_tokens(T)
+    say(f"[edges] mid_bf16 T={T}")
+    tens = inputs.generate(shape, seed=2, device=DEV)
+    blk, out = run_block(tens)
+    f = oracle_forward(tens)
+    gidx, gw = gpu_route(blk, shape, T)
+    bad, _ = route_check(shape, f.route, gidx, gw)
+    out_check(shape, to_np(out), f.out, skip=bad)
+
+
+def test_zero_tokens_is_noop():
+    shape = SMALL["mid_bf16"]
+    tens = inputs.generate(shape.with_tokens(4), seed=0, device=DEV)
+    blk = moe.Block(tens, 4)
+    out = torch.full_like(tens.x, 7.0)
+    moe.forward(blk.cfg, blk.wts, tens.x, out, blk.ws, tokens=0)
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
+
+
+def test_all_tokens_forced_into_one_group():
+    """+10 on every expert of group 3: that group is kept by every token and all K experts
+    (K <= group size) come from it."""
+    shape = SMALL["mid_bf16"]
+    tens = inputs.generate(shape, seed=3, device=DEV)
+    gs = shape.n_experts // shape.n_groups
+    tens.bias[3 * gs:4 * gs] += 10.0
+    blk, out = run_block(tens)
+    f = oracle_forward(tens)
+    gidx, gw = gpu_route(blk, shape, shape.tokens)
+    route_check(shape, f.route, gidx, gw)
+    assert ((gidx >= 3 * gs) & (gidx < 4 * gs)).all()
+    counts = gpu_dispatch(blk, shape, shape.tokens)[0]
+    assert (counts == 0).sum() >= shape.n_experts - gs
+    out_check(shape, to_np(out), f.out)
+
+
+def test_route_without_bias_uses_group_max():
+    """The excerpt's no-bias branch (bias NULL): groups scored by their best expert."""
+    shape = SMALL["mid_bf16"].replace(has_bias=False)
+    tens = inputs.generate(shape, seed=4, device=DEV)
+    cfg = moe.config(shape)
+    T, K = shape.tokens, shape.topk
+    ws = torch.empty(moe.workspace_size(cfg, T), dtype=torch.uint8, device=DEV)
+    idx = torch.empty(T, K, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, K, dtype=torch.float32, device=DEV)
+    moe.route(cfg, tens.w_gate, None, tens.x, idx, w, ws)
+    torch.cuda.synchronize()
+    r = O.route(shape, exact(tens.x), exact(tens.w_gate), None)
+    route_check(shape, r, np_i32(idx), w.cpu().numpy())
+
+
+@pytest.mark.parametrize("T,E,K", [(1, 256, 8), (1000, 256, 8), (3000, 64, 6), (513, 16, 4)])
+def test_dispatch_standalone(T, E, K):
+    shape = inputs.WORKLOADS["decode_bf16"].replace(n_experts=E, topk=K, n_groups=8 if E >= 64 else 4,
+                                                    topk_groups=4 if E >= 64 else 2)
+    rng = np.random.default_rng(T)
+    if E == 256:  # heavy skew: half the assignments on 8 experts
+        hot = rng.choice(E, 8, replace=False)
+        idx = np.stack([np.concatenate([rng.choice(hot, K // 2, replace=False),
+                                        rng.choice(np.setdiff1d(np.arange(E), hot), K - K // 2, replace=False)])
+                        for _ in range(T)])
+    else:
+        idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)])
+    cfg = moe.config(shape)
+    gi = torch.from_numpy(idx.astype(np.int32)).to(DEV)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    row_token = torch.empty(T * K, dtype=torch.int32, device=DEV)
+    row_of = torch.empty(T, K, dtype=torch.int32, device=DEV)
+    ws = torch.empty(moe.workspace_size(cfg, T), dtype=torch.uint8, device=DEV)
+    moe.dispatch(cfg, gi, counts, offsets, row_token, row_of, ws)
+    torch.cuda.synchronize()
+    dispatch_check(shape, idx, np_i32(counts), np_i32(offsets), np_i32(row_token), np_i32(row_of))
+
+
+def test_fp8_activation_codes_bit_exact():
+    shape = SMALL["mid_fp8"]
+    tens = inputs.generate(shape, seed=5, device=DEV)
+    blk, _ = run_block(tens)
+    T, D = shape.tokens, shape.dim
+    xq = blk.ws_view(T, "xq", torch.uint8, T * D).view(T, D).cpu().numpy()
+    sx = blk.ws_view(T, "x_scale", torch.float32, T * D // 128).view(T, D // 128).cpu().numpy()
+    q, sc = O.quant_1x128(exact(tens.x).astype(np.float32))
+    assert np.array_equal(sx, sc)
+    assert np.array_equal(O.e4m3_decode(xq), O.e4m3_decode(q))
+
+
+@pytest.mark.parametrize("name", ["mid_bf16", "mid_fp8"])
+def test_deterministic_reruns(name):
+    shape = SMALL[name]
+    tens = inputs.generate(shape, seed=6, device=DEV)
+    blk = moe.Block(tens, shape.tokens)
+    a = blk.forward(tens.x).clone()
+    ws_a = blk.ws.clone()
+    b = blk.forward(tens.x)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    lay = blk.layout(shape.tokens)
+    assert torch.equal(ws_a[lay.idx:lay.o_shared], blk.ws[lay.idx:lay.o_shared])
