@@ -25,7 +25,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   moe_ws_layout pub;
-  size_t meta, blk, tiles_s, tiles_w, zpart;
+  size_t meta, blk, tiles_s, tiles_w, zpart, z32;
   int nsplit;
 };
 
@@ -90,6 +90,7 @@ Layout plan(const moe::Dims& d) {
   L.tiles_w = take((size_t)moe::max_tiles(d, moe::kWideBM) * sizeof(Tile));
   L.nsplit = moe::router_splits(d);
   L.zpart = take((size_t)L.nsplit * d.T * d.E * 8);
+  L.z32 = take((size_t)d.T * d.E * 4);
   L.pub.xq = take(fp8 ? (size_t)d.T * d.D : 0);
   L.pub.x_scale = take(fp8 ? (size_t)d.T * (d.D / 128) * 4 : 0);
   L.pub.h_routed = take((size_t)d.R * d.I * act);
@@ -255,7 +256,7 @@ moe_status moe_route(const moe_config* cfg, const void* w_gate, const float* bia
   double* zpart = at<double>(ws, L.zpart);
   if ((st = hip_status(moe::launch_router_logits(d, x, w_gate, zpart, L.nsplit, s), "router logits")) != MOE_OK)
     return st;
-  return hip_status(moe::launch_router_select(d, zpart, L.nsplit, bias, cfg->route_scale, idx, w, s),
+  return hip_status(moe::launch_router_select(d, zpart, L.nsplit, at<float>(ws, L.z32), bias, cfg->route_scale, idx, w, s),
                     "router select");
 }
 
@@ -310,7 +311,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wts, const void
     return st;
   if ((st = hip_status(moe::launch_router_logits(d, x, wts->w_gate, zpart, L.nsplit, s), "router logits")) != MOE_OK)
     return st;
-  if ((st = hip_status(moe::launch_router_select(d, zpart, L.nsplit, wts->bias, cfg->route_scale, idx, w, s),
+  if ((st = hip_status(moe::launch_router_select(d, zpart, L.nsplit, at<float>(ws, L.z32), wts->bias, cfg->route_scale, idx, w, s),
                        "router select")) != MOE_OK)
     return st;
   if ((st = hip_status(moe::launch_dispatch(d, idx, at<int32_t>(ws, L.blk), at<int32_t>(ws, L.pub.counts), offsets,

@@ -64,7 +64,8 @@ MOE_DEV float wave_max(float v) {
 }
 
 // Tile of rows handled by one GEMM work item: `expert` (E = the shared expert),
-// first row (routed: dispatch row; shared: token) and number of rows.
+// first row (routed: dispatch row; shared: token), number of rows, and the index of
+// the expert's first tile in the list.
 struct Tile {
-  int expert, row0, nrows, pad;
+  int expert, row0, nrows, first;
 };

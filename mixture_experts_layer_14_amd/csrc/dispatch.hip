@@ -82,12 +82,13 @@ __device__ void write_tiles(const int* cnt, const int* off, int E, int T, int bm
     int e = threadIdx.x * per + j;
     if (e >= E) break;
     int c = cnt[e];
+    const int first = base;
     for (int m = 0; m < c; m += bm) {
       Tile tl;
       tl.expert = e;
       tl.row0 = off[e] + m;
       tl.nrows = min(bm, c - m);
-      tl.pad = 0;
+      tl.first = first;
       tiles[base++] = tl;
     }
   }
@@ -97,7 +98,7 @@ __device__ void write_tiles(const int* cnt, const int* off, int E, int T, int bm
     tl.expert = E;
     tl.row0 = j * bm;
     tl.nrows = min(bm, T - j * bm);
-    tl.pad = 0;
+    tl.first = total;
     tiles[total + j] = tl;
   }
   if (threadIdx.x == 0) {

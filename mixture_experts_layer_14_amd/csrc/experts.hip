@@ -5,6 +5,8 @@
 // A is x gathered through the dispatch permutation (routed rows) or x itself (shared
 // expert, tile expert index E). Work comes from the device-side tile lists the dispatch
 // wrote, so experts with no tokens are never read and the host never waits.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace moe {
@@ -426,6 +428,8 @@ hipError_t launch_experts(const Dims& d, const ExpertPtrs& w, const Act& a, hipS
     return hipGetLastError();
   }
   const int64_t tiles16 = max_tiles(d, kSkinnyBM);
+  // 128-row tiles once the routed experts average 16 rows or more
+  if (d.dtype == 1 && wide_ok(d) && d.R >= 16 * (int64_t)d.E) return launch_wide_bf16(d, w, a, s);
   if (d.dtype == 1) {
     int64_t it1 = tiles16 * (d.S > d.I ? d.S : d.I) / 16;
     int64_t it2 = tiles16 * (d.D / 64);

@@ -45,7 +45,8 @@ struct Dims {
 int router_splits(const Dims& d);
 hipError_t launch_router_logits(const Dims& d, const void* x, const void* w_gate, double* zpart, int nsplit,
                                 hipStream_t s);
-hipError_t launch_router_select(const Dims& d, const double* zpart, int nsplit, const float* bias,
+// nsplit > 1: a reduce kernel sums the slices into z32 [T, E] first.
+hipError_t launch_router_select(const Dims& d, const double* zpart, int nsplit, float* z32, const float* bias,
                                 float route_scale, int32_t* idx, float* w, hipStream_t s);
 
 // ---- dispatch
@@ -79,6 +80,9 @@ struct Act {
   void* o_shared;           // [T, D]
 };
 hipError_t launch_experts(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
+// 128-row LDS-tiled bf16 kernels (prefill-sized batches)
+bool wide_ok(const Dims& d);
+hipError_t launch_wide_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
 
 // ---- combine
 hipError_t launch_combine(const Dims& d, const int32_t* idx, const float* w, const int32_t* row_of,

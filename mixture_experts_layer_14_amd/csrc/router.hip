@@ -13,7 +13,7 @@ namespace moe {
 // fp32, chunk sum rounded once) and the chunks are summed in fp64, so z keeps
 // well under 1e-7 absolute error before its single rounding to fp32. Partial
 // sums over `nsplit` slices of D are written to zpart[split][T][E] (fp64) and
-// added in split order by the selection kernel.
+// added in split order by router_reduce.
 //
 // Block: 4 waves; wave tile 32 tokens x 32 experts (2 x 2 MFMA tiles); block
 // tile 32 tokens x 128 experts. Grid (T/32, E/128, nsplit).
@@ -85,6 +85,16 @@ __global__ __launch_bounds__(256) void router_logits_bf16(const bf16_t* __restri
     }
 }
 
+// Sum the per-slice fp64 partial logits in slice order and round once to fp32.
+__global__ __launch_bounds__(256) void router_reduce(const double* __restrict__ zpart, int nsplit, int64_t n,
+                                                     float* __restrict__ z) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  double acc = 0.0;
+  for (int p = 0; p < nsplit; ++p) acc += zpart[(size_t)p * n + i];
+  z[i] = (float)acc;
+}
+
 // fp32 inputs: each product is exact in fp64; one thread per (token, expert).
 __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict__ x, const float* __restrict__ wg,
                                                          double* __restrict__ zpart, int T, int D, int E) {
@@ -105,7 +115,7 @@ __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict
 // ---------------------------------------------------------------------------
 constexpr int kMaxE = 1024, kMaxG = 64, kMaxK = 16;
 
-__global__ __launch_bounds__(256) void router_select(const double* __restrict__ zpart, int nsplit,
+__global__ __launch_bounds__(256) void router_select(const double* __restrict__ zpart, const float* __restrict__ z32,
                                                      const float* __restrict__ bias, int T, int E, int G, int Gk,
                                                      int K, float route_scale, int32_t* __restrict__ idx_out,
                                                      float* __restrict__ w_out) {
@@ -122,9 +132,7 @@ __global__ __launch_bounds__(256) void router_select(const double* __restrict__ 
 
   if (active) {
     for (int e = lane; e < E; e += 64) {
-      double z = 0.0;
-      for (int p = 0; p < nsplit; ++p) z += zpart[((size_t)p * T + t) * E + e];
-      float zf = (float)z;
+      const float zf = z32 ? z32[(size_t)t * E + e] : (float)zpart[(size_t)t * E + e];
       float sv = (float)(1.0 / (1.0 + exp(-(double)zf)));
       s[e] = sv;
       sb[e] = bias ? sv + bias[e] : sv;
@@ -240,11 +248,17 @@ hipError_t launch_router_logits(const Dims& d, const void* x, const void* w_gate
   return hipGetLastError();
 }
 
-hipError_t launch_router_select(const Dims& d, const double* zpart, int nsplit, const float* bias,
+hipError_t launch_router_select(const Dims& d, const double* zpart, int nsplit, float* z32, const float* bias,
                                 float route_scale, int32_t* idx, float* w, hipStream_t s) {
   if (d.T == 0) return hipSuccess;
+  const float* zf = nullptr;
+  if (nsplit > 1) {
+    int64_t n = d.T * d.E;
+    MOE_LAUNCH(router_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, zpart, nsplit, n, z32);
+    zf = z32;
+  }
   size_t lds = 4 * (2 * (size_t)d.E + 2 * kMaxG) * sizeof(float);
-  MOE_LAUNCH(router_select, dim3((unsigned)((d.T + 3) / 4)), dim3(256), lds, s, zpart, nsplit, bias,
+  MOE_LAUNCH(router_select, dim3((unsigned)((d.T + 3) / 4)), dim3(256), lds, s, zpart, zf, bias,
                      (int)d.T, d.E, d.G, d.Gk, d.K, route_scale, idx, w);
   return hipGetLastError();
 }
