@@ -154,6 +154,24 @@ void drop_spans() {
 }  // namespace
 
 namespace moe {
+int persistent_grid(const void* kernel, int threads, size_t dyn_lds) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::lock_guard<std::mutex> lk(mu);
+  auto key = std::make_pair(dev, kernel);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn_lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  const int g = per_cu * cus;
+  cache[key] = g;
+  return g;
+}
+
 void span_begin(const char* name, hipStream_t s) {
   if (!g_timing) return;
   std::lock_guard<std::mutex> lk(g_tmu);

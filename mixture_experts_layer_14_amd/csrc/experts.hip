@@ -11,8 +11,7 @@
 
 namespace moe {
 
-// Occupancy-sized persistent grids.
-constexpr int kPersistBlocks = 256 * 8;
+constexpr int kPersistBlocks = 256 * 8;  // grid cap of the fp32 kernels
 
 __device__ __forceinline__ int n_items(const int32_t* meta, int list, int per_routed, int per_shared) {
   int nr = meta[2 * list], na = meta[2 * list + 1];
@@ -31,132 +30,6 @@ __device__ __forceinline__ void split_item(int item, const int32_t* meta, int li
     int j = item - routed_items;
     *tile = nr + j / per_shared;
     *nt = j % per_shared;
-  }
-}
-
-// ===========================================================================
-// bf16, M-tiles of 16 rows (decode and thin experts): the weights stream straight
-// from HBM into MFMA operands, every byte read once per M-tile.
-// ===========================================================================
-
-// Item: 16 rows x 16 h-columns; the 4 waves split K = D in quarters and the partial
-// accumulators are reduced through LDS in wave order.
-__global__ __launch_bounds__(256) void gemm1_bf16_m16(const bf16_t* __restrict__ x, const int32_t* __restrict__ row_token,
-                                                      const Tile* __restrict__ tiles, const int32_t* __restrict__ meta,
-                                                      const bf16_t* __restrict__ w1, const bf16_t* __restrict__ w3,
-                                                      const bf16_t* __restrict__ ws1, const bf16_t* __restrict__ ws3,
-                                                      bf16_t* __restrict__ h_routed, bf16_t* __restrict__ h_shared,
-                                                      int D, int I, int S, int E) {
-  __shared__ f32x4 red[4][2][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 15, kq = lane >> 4;
-  const int per_r = I / 16, per_s = S / 16;
-  const int items = n_items(meta, 0, per_r, per_s);
-  const int kq_len = D / 4;
-  const i32x4 zero = {0, 0, 0, 0};
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    int ti, nt;
-    split_item(item, meta, 0, per_r, per_s, &ti, &nt);
-    const Tile tl = tiles[ti];
-    const bool sh = tl.expert == E;
-    const int ld_w = D;
-    const bf16_t* W1 = sh ? ws1 : w1 + (size_t)tl.expert * I * D;
-    const bf16_t* W3 = sh ? ws3 : w3 + (size_t)tl.expert * I * D;
-    const int n0 = nt * 16;
-    const bool av = r < tl.nrows;
-    int tok = 0;
-    if (av) tok = sh ? tl.row0 + r : row_token[tl.row0 + r];
-    const int kbeg = wave * kq_len;
-    const bf16_t* ap = x + (size_t)tok * D + kbeg + kq * 8;
-    const bf16_t* b1p = W1 + (size_t)(n0 + r) * ld_w + kbeg + kq * 8;
-    const bf16_t* b3p = W3 + (size_t)(n0 + r) * ld_w + kbeg + kq * 8;
-    f32x4 g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
-    int k = 0;
-    for (; k + 128 <= kq_len; k += 128) {
-      i32x4 a[4], b1[4], b3[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        b1[j] = ld16(b1p + k + 32 * j);
-        b3[j] = ld16(b3p + k + 32 * j);
-        a[j] = av ? ld16(ap + k + 32 * j) : zero;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        g = mfma_bf16_16x16x32(a[j], b1[j], g);
-        u = mfma_bf16_16x16x32(a[j], b3[j], u);
-      }
-    }
-    for (; k < kq_len; k += 32) {
-      i32x4 a = av ? ld16(ap + k) : zero;
-      g = mfma_bf16_16x16x32(a, ld16(b1p + k), g);
-      u = mfma_bf16_16x16x32(a, ld16(b3p + k), u);
-    }
-    red[wave][0][lane] = g;
-    red[wave][1][lane] = u;
-    __syncthreads();
-    if (wave == 0) {
-      f32x4 gs = red[0][0][lane], us = red[0][1][lane];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) {
-        gs += red[w][0][lane];
-        us += red[w][1][lane];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int row = kq * 4 + i;
-        if (row < tl.nrows) {
-          float hv = silu_mul(gs[i], us[i]);
-          bf16_t* dst = sh ? h_shared + (size_t)(tl.row0 + row) * S : h_routed + (size_t)(tl.row0 + row) * I;
-          dst[n0 + r] = f32_to_bf16(hv);
-        }
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// Item: 16 rows x 64 output columns; each wave owns 16 columns over the full K = I.
-__global__ __launch_bounds__(256) void gemm2_bf16_m16(const bf16_t* __restrict__ h_routed,
-                                                      const bf16_t* __restrict__ h_shared, const Tile* __restrict__ tiles,
-                                                      const int32_t* __restrict__ meta, const bf16_t* __restrict__ w2,
-                                                      const bf16_t* __restrict__ ws2, bf16_t* __restrict__ o_routed,
-                                                      bf16_t* __restrict__ o_shared, int D, int I, int S, int E) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 15, kq = lane >> 4;
-  const int per = D / 64;
-  const int items = n_items(meta, 0, per, per);
-  const i32x4 zero = {0, 0, 0, 0};
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    int ti, nt;
-    split_item(item, meta, 0, per, per, &ti, &nt);
-    const Tile tl = tiles[ti];
-    const bool sh = tl.expert == E;
-    const int KK = sh ? S : I;
-    const bf16_t* A = sh ? h_shared + (size_t)tl.row0 * S : h_routed + (size_t)tl.row0 * I;
-    const bf16_t* W = sh ? ws2 : w2 + (size_t)tl.expert * D * I;
-    const int c0 = nt * 64 + wave * 16;
-    const bool av = r < tl.nrows;
-    const bf16_t* ap = A + (size_t)(av ? r : 0) * KK + kq * 8;
-    const bf16_t* bp = W + (size_t)(c0 + r) * KK + kq * 8;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int k = 0;
-    for (; k + 128 <= KK; k += 128) {
-      i32x4 a[4], b[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        b[j] = ld16(bp + k + 32 * j);
-        a[j] = av ? ld16(ap + k + 32 * j) : zero;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc = mfma_bf16_16x16x32(a[j], b[j], acc);
-    }
-    for (; k < KK; k += 32) acc = mfma_bf16_16x16x32(av ? ld16(ap + k) : zero, ld16(bp + k), acc);
-    bf16_t* O = sh ? o_shared : o_routed;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int row = kq * 4 + i;
-      if (row < tl.nrows) O[(size_t)(tl.row0 + row) * D + c0 + r] = f32_to_bf16(acc[i]);
-    }
   }
 }
 
@@ -427,29 +300,18 @@ hipError_t launch_experts(const Dims& d, const ExpertPtrs& w, const Act& a, hipS
                        (float*)a.o_routed, (float*)a.o_shared, d.R, d.T, d.D, d.I, d.S, E);
     return hipGetLastError();
   }
-  const int64_t tiles16 = max_tiles(d, kSkinnyBM);
-  // 128-row tiles once the routed experts average 16 rows or more
-  if (d.dtype == 1 && wide_ok(d) && d.R >= 16 * (int64_t)d.E) return launch_wide_bf16(d, w, a, s);
   if (d.dtype == 1) {
-    int64_t it1 = tiles16 * (d.S > d.I ? d.S : d.I) / 16;
-    int64_t it2 = tiles16 * (d.D / 64);
-    MOE_LAUNCH(gemm1_bf16_m16, dim3((unsigned)std::min<int64_t>(it1, kPersistBlocks)), dim3(256), 0, s,
-                       (const bf16_t*)a.x, a.row_token, a.tiles_skinny, a.meta, (const bf16_t*)w.w1,
-                       (const bf16_t*)w.w3, (const bf16_t*)w.ws1, (const bf16_t*)w.ws3, (bf16_t*)a.h_routed,
-                       (bf16_t*)a.h_shared, d.D, d.I, d.S, E);
-    MOE_LAUNCH(gemm2_bf16_m16, dim3((unsigned)std::min<int64_t>(it2, kPersistBlocks)), dim3(256), 0, s,
-                       (const bf16_t*)a.h_routed, (const bf16_t*)a.h_shared, a.tiles_skinny, a.meta,
-                       (const bf16_t*)w.w2, (const bf16_t*)w.ws2, (bf16_t*)a.o_routed, (bf16_t*)a.o_shared, d.D,
-                       d.I, d.S, E);
-    return hipGetLastError();
+    // 128-row tiles once the routed experts average 16 rows or more
+    if (wide_ok(d) && d.R >= 16 * (int64_t)d.E) return launch_wide_bf16(d, w, a, s);
+    return launch_stream_bf16(d, w, a, s);
   }
-  int64_t it1 = tiles16 * (d.S > d.I ? d.S : d.I) / 128;
-  int64_t it2 = tiles16 * (d.D / 64);
-  MOE_LAUNCH(gemm1_fp8_m16, dim3((unsigned)std::min<int64_t>(it1, kPersistBlocks)), dim3(256), 0, s,
+  const int g1 = persistent_grid((const void*)gemm1_fp8_m16, 256);
+  const int g2 = persistent_grid((const void*)gemm2_fp8_m16, 256);
+  MOE_LAUNCH(gemm1_fp8_m16, dim3(g1), dim3(256), 0, s,
                      (const uint8_t*)a.x, a.x_scale, a.row_token, a.tiles_skinny, a.meta, (const uint8_t*)w.w1,
                      (const uint8_t*)w.w3, w.s1, w.s3, (const uint8_t*)w.ws1, (const uint8_t*)w.ws3, w.ss1, w.ss3,
                      (uint8_t*)a.h_routed, a.h_scale, (uint8_t*)a.h_shared, a.h_shared_scale, d.D, d.I, d.S, E);
-  MOE_LAUNCH(gemm2_fp8_m16, dim3((unsigned)std::min<int64_t>(it2, kPersistBlocks)), dim3(256), 0, s,
+  MOE_LAUNCH(gemm2_fp8_m16, dim3(g2), dim3(256), 0, s,
                      (const uint8_t*)a.h_routed, a.h_scale, (const uint8_t*)a.h_shared, a.h_shared_scale,
                      a.tiles_skinny, a.meta, (const uint8_t*)w.w2, w.s2, (const uint8_t*)w.ws2, w.ss2,
                      (bf16_t*)a.o_routed, (bf16_t*)a.o_shared, d.D, d.I, d.S, E);

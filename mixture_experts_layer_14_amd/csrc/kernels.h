@@ -80,6 +80,10 @@ struct Act {
   void* o_shared;           // [T, D]
 };
 hipError_t launch_experts(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
+// 16-row weight-streaming bf16 kernels (decode-sized batches)
+hipError_t launch_stream_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
+// Blocks of `kernel` that fit on the current device at once (occupancy x CUs), cached.
+int persistent_grid(const void* kernel, int threads, size_t dyn_lds = 0);
 // 128-row LDS-tiled bf16 kernels (prefill-sized batches)
 bool wide_ok(const Dims& d);
 hipError_t launch_wide_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
