@@ -7,6 +7,8 @@
 // Also the per-token 1x128 activation quantisation for fp8 blocks.
 #include <math.h>
 
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace moe {
@@ -50,21 +52,27 @@ __global__ __launch_bounds__(256) void combine(const int32_t* __restrict__ idx, 
     const bf16_t* O = static_cast<const bf16_t*>(o_routed);
     const bf16_t* SH = static_cast<const bf16_t*>(o_shared) + (size_t)t * D;
     bf16_t* Y = static_cast<bf16_t*>(out) + (size_t)t * D;
-    for (int c = threadIdx.x * 8; c < D; c += 256 * 8) {
+    for (int c = (blockIdx.y * 256 + threadIdx.x) * 8; c < D; c += gridDim.y * 256 * 8) {
       float y[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = 0.f;
-      for (int k = 0; k < K; ++k) {
-        i32x4 v = ld16(O + (size_t)srow[k] * D + c);
+      // all rows are loaded before the in-order accumulation
+      i32x4 rows[kMaxTopK];
+#pragma unroll
+      for (int k = 0; k < kMaxTopK; ++k)
+        if (k < K) rows[k] = ld16(O + (size_t)srow[k] * D + c);
+      i32x4 v = ld16(SH + c);
+#pragma unroll
+      for (int k = 0; k < kMaxTopK; ++k) {
+        if (k >= K) continue;
         const float wk = sw[k];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          uint32_t p = (uint32_t)v[j];
+          uint32_t p = (uint32_t)rows[k][j];
           y[2 * j] = y[2 * j] + bf16_to_f32((bf16_t)(p & 0xFFFF)) * wk;
           y[2 * j + 1] = y[2 * j + 1] + bf16_to_f32((bf16_t)(p >> 16)) * wk;
         }
       }
-      i32x4 v = ld16(SH + c);
       i32x4 res;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -79,7 +87,7 @@ __global__ __launch_bounds__(256) void combine(const int32_t* __restrict__ idx, 
     const float* O = static_cast<const float*>(o_routed);
     const float* SH = static_cast<const float*>(o_shared) + (size_t)t * D;
     float* Y = static_cast<float*>(out) + (size_t)t * D;
-    for (int c = threadIdx.x; c < D; c += 256) {
+    for (int c = blockIdx.y * 256 + threadIdx.x; c < D; c += gridDim.y * 256) {
       float y = 0.f;
       for (int k = 0; k < K; ++k) y = y + O[(size_t)srow[k] * D + c] * sw[k];
       Y[c] = y + SH[c];
@@ -106,12 +114,14 @@ __global__ __launch_bounds__(256) void act_quant(const bf16_t* __restrict__ x, u
 hipError_t launch_combine(const Dims& d, const int32_t* idx, const float* w, const int32_t* row_of,
                           const void* o_routed, const void* o_shared, void* out, hipStream_t s) {
   if (d.T == 0) return hipSuccess;
+  // split the columns over more blocks when there are few tokens
+  const unsigned ysplit = d.T >= 1024 ? 1u : (unsigned)std::max(1, std::min(8, d.D / 2048));
   if (d.dtype == 0)
-    MOE_LAUNCH(combine<false>, dim3((unsigned)d.T), dim3(256), 0, s, idx, w, row_of, o_routed, o_shared, out,
-                       d.K, d.D);
+    MOE_LAUNCH(combine<false>, dim3((unsigned)d.T, ysplit), dim3(256), 0, s, idx, w, row_of, o_routed, o_shared,
+               out, d.K, d.D);
   else
-    MOE_LAUNCH(combine<true>, dim3((unsigned)d.T), dim3(256), 0, s, idx, w, row_of, o_routed, o_shared, out,
-                       d.K, d.D);
+    MOE_LAUNCH(combine<true>, dim3((unsigned)d.T, ysplit), dim3(256), 0, s, idx, w, row_of, o_routed, o_shared,
+               out, d.K, d.D);
   return hipGetLastError();
 }
 

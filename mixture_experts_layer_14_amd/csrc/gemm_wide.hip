@@ -33,40 +33,6 @@ MOE_DEV f32x16 mfma32(i32x4 a, i32x4 b, f32x16 c) {
                                                  0, 0, 0);
 }
 
-MOE_DEV int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
-
-struct WideItem {
-  Tile tl;
-  int nt;
-  bool shared;
-};
-
-// item -> (tile, n-tile): routed items first (per_r n-tiles per expert), then the shared
-// expert's (per_s). Within an expert: n-tile major, m-tile minor.
-MOE_DEV WideItem wide_item(int item, const Tile* __restrict__ tiles, const int32_t* __restrict__ meta,
-                           const int32_t* __restrict__ offsets, int T, int E, int per_r, int per_s) {
-  const int nr = meta[2], na = meta[3];
-  WideItem w;
-  int per = per_r, base_tiles = 0, local_item = item;
-  if (item >= nr * per_r) {
-    per = per_s;
-    base_tiles = nr;
-    local_item = item - nr * per_r;
-  }
-  const int q = base_tiles + local_item / per;  // a tile of the right expert
-  const Tile probe = tiles[q];
-  const int first = probe.first;
-  const int e = probe.expert;
-  const int rows = e == E ? T : offsets[e + 1] - offsets[e];
-  const int mt = (rows + WBM - 1) / WBM;
-  const int local = item - (first - base_tiles) * per - (base_tiles ? nr * per_r : 0);
-  w.nt = local / mt;
-  w.tl = tiles[first + local % mt];
-  w.shared = e == E;
-  (void)na;
-  return w;
-}
-
 template <int MODE>
 __global__ __launch_bounds__(256, kWideBlocksPerCU) void gemm_wide_bf16(
     const bf16_t* __restrict__ act_x, const bf16_t* __restrict__ h_routed_in, const bf16_t* __restrict__ h_shared_in,

@@ -84,6 +84,9 @@ hipError_t launch_experts(const Dims& d, const ExpertPtrs& w, const Act& a, hipS
 hipError_t launch_stream_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
 // Blocks of `kernel` that fit on the current device at once (occupancy x CUs), cached.
 int persistent_grid(const void* kernel, int threads, size_t dyn_lds = 0);
+// 128-row LDS-tiled fp8 kernels with 128-k scale promotion (prefill-sized batches)
+bool wide_fp8_ok(const Dims& d);
+hipError_t launch_wide_fp8(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
 // 128-row LDS-tiled bf16 kernels (prefill-sized batches)
 bool wide_ok(const Dims& d);
 hipError_t launch_wide_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
@@ -91,5 +94,41 @@ hipError_t launch_wide_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hi
 // ---- combine
 hipError_t launch_combine(const Dims& d, const int32_t* idx, const float* w, const int32_t* row_of,
                           const void* o_routed, const void* o_shared, void* out, hipStream_t s);
+
+// ---- device helpers shared by the 128-row (wide) kernels
+// LDS tile rows are 128 bytes; 16-byte chunks are XOR-swizzled by (row % 8).
+MOE_DEV int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+struct WideItem {
+  Tile tl;
+  int nt;
+  bool shared;
+};
+
+// item -> (tile, n-tile): routed items first (per_r n-tiles per expert), then the shared
+// expert's (per_s). Within an expert: n-tile major, m-tile minor.
+MOE_DEV WideItem wide_item(int item, const Tile* __restrict__ tiles, const int32_t* __restrict__ meta,
+                           const int32_t* __restrict__ offsets, int T, int E, int per_r, int per_s) {
+  const int nr = meta[2], na = meta[3];
+  WideItem w;
+  int per = per_r, base_tiles = 0, local_item = item;
+  if (item >= nr * per_r) {
+    per = per_s;
+    base_tiles = nr;
+    local_item = item - nr * per_r;
+  }
+  const int q = base_tiles + local_item / per;  // a tile of the right expert
+  const Tile probe = tiles[q];
+  const int first = probe.first;
+  const int e = probe.expert;
+  const int rows = e == E ? T : offsets[e + 1] - offsets[e];
+  const int mt = (rows + kWideBM - 1) / kWideBM;
+  const int local = item - (first - base_tiles) * per - (base_tiles ? nr * per_r : 0);
+  w.nt = local / mt;
+  w.tl = tiles[first + local % mt];
+  w.shared = e == E;
+  (void)na;
+  return w;
+}
 
 }  // namespace moe

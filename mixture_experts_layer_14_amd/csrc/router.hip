@@ -4,6 +4,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace moe {
@@ -90,8 +92,13 @@ __global__ __launch_bounds__(256) void router_reduce(const double* __restrict__ 
                                                      float* __restrict__ z) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
+  double part[16];
+#pragma unroll
+  for (int p = 0; p < 16; ++p) part[p] = p < nsplit ? zpart[(size_t)p * n + i] : 0.0;
   double acc = 0.0;
-  for (int p = 0; p < nsplit; ++p) acc += zpart[(size_t)p * n + i];
+#pragma unroll
+  for (int p = 0; p < 16; ++p)
+    if (p < nsplit) acc += part[p];
   z[i] = (float)acc;
 }
 
@@ -220,8 +227,9 @@ int router_splits(const Dims& d) {
   if (d.dtype == 0) return 1;
   int64_t row_tiles = (d.T + 31) / 32;
   int64_t col_tiles = (d.E + 127) / 128;
-  int64_t want = (512 + row_tiles * col_tiles - 1) / (row_tiles * col_tiles);
-  int64_t max_split = d.D / 64;
+  // enough blocks to stream the router weight with many CUs, but few slices to add up
+  int64_t want = (256 + row_tiles * col_tiles - 1) / (row_tiles * col_tiles);
+  int64_t max_split = std::min<int64_t>(16, d.D / 64);
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;
   return (int)want;

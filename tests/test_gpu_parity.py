@@ -94,10 +94,11 @@ def test_forward_full_shape(name):
         say(f"  fraction of assignments on the 32 biased experts: {hot:.4f}")
 
 
-@pytest.mark.parametrize("T", [1, 17, 64])
-def test_token_counts_edges(T):
-    shape = SMALL["mid_bf16"].with_tokens(T)
-    say(f"[edges] mid_bf16 T={T}")
+@pytest.mark.parametrize("name,T", [("mid_bf16", 1), ("mid_bf16", 17), ("mid_bf16", 64), ("mid_fp8", 3),
+                                    ("mid_fp8", 40), ("mid_fp8", 129)])
+def test_token_counts_edges(name, T):
+    shape = SMALL[name].with_tokens(T)
+    say(f"[edges] {name} T={T}")
     tens = inputs.generate(shape, seed=2, device=DEV)
     blk, out = run_block(tens)
     f = oracle_forward(tens)
