@@ -36,6 +36,9 @@ def parse():
     p.add_argument("--workload", default="decode_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--calib-copy-mb", type=int, default=0,
+                   help="first run a plain device copy of this many MiB (the reference kernel for scaling "
+                        "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
     return p.parse_args()
 
 
@@ -109,6 +112,14 @@ def main():
     shape = inputs.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    if args.calib_copy_mb:
+        src = torch.ones(args.calib_copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {args.calib_copy_mb} MiB x 3 done", file=sys.stderr, flush=True)
+        del src, dst
     print(f"[bench] generating {shape.name} inputs (seed {args.seed})", file=sys.stderr, flush=True)
     tens = inputs.generate(shape, seed=args.seed, device=dev)
     blk = moe.Block(tens, shape.tokens)
