@@ -149,7 +149,7 @@ def main():
     kernels = {name: (cnt, tot / cnt) for name, (cnt, tot) in kt.items()}
     dom = max(kernels, key=lambda n: kernels[n][0] * kernels[n][1])
     dom_ms = kernels[dom][1]
-    kind = "gemm1" if ("gemm1" in dom or "<0>" in dom) else ("gemm2" if ("gemm2" in dom or "<1>" in dom) else None)
+    kind = "gemm1" if ("gemm1" in dom or "<0" in dom) else ("gemm2" if ("gemm2" in dom or "<1" in dom) else None)
     decode_like = T <= 256
     roof = None
     if kind:

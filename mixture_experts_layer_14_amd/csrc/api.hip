@@ -25,7 +25,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   moe_ws_layout pub;
-  size_t meta, blk, tiles_s, tiles_w, zpart, z32;
+  size_t meta, blk, tiles_s, tiles_w, tiles_w2, zpart, z32;
   int nsplit;
 };
 
@@ -88,6 +88,7 @@ Layout plan(const moe::Dims& d) {
   L.blk = take((size_t)std::max(1, moe::dispatch_blocks(d.T)) * d.E * 4);
   L.tiles_s = take((size_t)moe::max_tiles(d, moe::kSkinnyBM) * sizeof(Tile));
   L.tiles_w = take((size_t)moe::max_tiles(d, moe::kWideBM) * sizeof(Tile));
+  L.tiles_w2 = take((size_t)moe::max_tiles(d, moe::kWideBM2) * sizeof(Tile));
   L.nsplit = moe::router_splits(d);
   L.zpart = take((size_t)L.nsplit * d.T * d.E * 8);
   L.z32 = take((size_t)d.T * d.E * 4);
@@ -290,7 +291,7 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* idx, int64_t T, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(moe::launch_dispatch(d, idx, at<int32_t>(ws, L.blk), counts, offsets, row_token, row_of,
                                          at<int32_t>(ws, L.meta), at<Tile>(ws, L.tiles_s),
-                                         at<Tile>(ws, L.tiles_w), s),
+                                         at<Tile>(ws, L.tiles_w), at<Tile>(ws, L.tiles_w2), s),
                     "dispatch");
 }
 
@@ -334,7 +335,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wts, const void
     return st;
   if ((st = hip_status(moe::launch_dispatch(d, idx, at<int32_t>(ws, L.blk), at<int32_t>(ws, L.pub.counts), offsets,
                                             row_token, row_of, meta, at<Tile>(ws, L.tiles_s),
-                                            at<Tile>(ws, L.tiles_w), s),
+                                            at<Tile>(ws, L.tiles_w), at<Tile>(ws, L.tiles_w2), s),
                        "dispatch")) != MOE_OK)
     return st;
   moe::ExpertPtrs ep{wts->w1, wts->w3, wts->w2, wts->ws1, wts->ws3, wts->ws2,
@@ -347,6 +348,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wts, const void
   act.meta = meta;
   act.tiles_skinny = at<Tile>(ws, L.tiles_s);
   act.tiles_wide = at<Tile>(ws, L.tiles_w);
+  act.tiles_wide2 = at<Tile>(ws, L.tiles_w2);
   act.h_routed = at<void>(ws, L.pub.h_routed);
   act.h_shared = at<void>(ws, L.pub.h_shared);
   act.h_scale = fp8 ? at<float>(ws, L.pub.h_scale) : nullptr;

@@ -6,7 +6,7 @@
 // Three launches over blocks of 256 tokens:
 //   count:   per block, an LDS bitmap bits[e][256 tokens] -> blk[b][e] = popcount
 //   scan:    one workgroup: blk[b][e] -> base row of block b inside expert e,
-//            counts, offsets, and the GEMM tile lists (M-tiles of 16 and 128 rows)
+//            counts, offsets, and the GEMM tile lists (M-tiles of 16, 128 and 256 rows)
 //   scatter: rebuilds the bitmap; row = base + popcount of earlier tokens' bits
 #include "kernels.h"
 
@@ -110,7 +110,7 @@ __device__ void write_tiles(const int* cnt, const int* off, int E, int T, int bm
 __global__ __launch_bounds__(256) void dispatch_scan(int32_t* __restrict__ blk, int nblk, int E, int T,
                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ meta, Tile* __restrict__ tiles_s,
-                                                     Tile* __restrict__ tiles_w) {
+                                                     Tile* __restrict__ tiles_w, Tile* __restrict__ tiles_w2) {
   __shared__ int cnt[1024];
   __shared__ int off[1025];
   __shared__ int scratch[4];
@@ -156,6 +156,8 @@ __global__ __launch_bounds__(256) void dispatch_scan(int32_t* __restrict__ blk, 
   write_tiles(cnt, off, E, T, kSkinnyBM, tiles_s, &meta[0], &meta[1], scratch);
   __syncthreads();
   write_tiles(cnt, off, E, T, kWideBM, tiles_w, &meta[2], &meta[3], scratch);
+  __syncthreads();
+  write_tiles(cnt, off, E, T, kWideBM2, tiles_w2, &meta[5], &meta[6], scratch);
   if (threadIdx.x == 0) meta[4] = nact;
 }
 
@@ -185,14 +187,14 @@ int64_t max_tiles(const Dims& d, int bm) { return d.R / bm + d.E + (d.T + bm - 1
 
 hipError_t launch_dispatch(const Dims& d, const int32_t* idx, int32_t* blk, int32_t* counts, int32_t* offsets,
                            int32_t* row_token, int32_t* row_of, int32_t* meta, Tile* tiles_s, Tile* tiles_w,
-                           hipStream_t s) {
+                           Tile* tiles_w2, hipStream_t s) {
   int nblk = dispatch_blocks(d.T);
   size_t lds = (size_t)d.E * WORDS * sizeof(unsigned long long);
   if (nblk > 0) {
     MOE_LAUNCH(dispatch_count, dim3(nblk), dim3(TB), lds, s, idx, (int)d.T, d.K, d.E, blk);
   }
   MOE_LAUNCH(dispatch_scan, dim3(1), dim3(256), 0, s, blk, nblk, d.E, (int)d.T, counts, offsets, meta,
-                     tiles_s, tiles_w);
+                     tiles_s, tiles_w, tiles_w2);
   if (nblk > 0) {
     MOE_LAUNCH(dispatch_scatter, dim3(nblk), dim3(TB), lds, s, idx, (int)d.T, d.K, d.E, blk, row_token,
                        row_of);

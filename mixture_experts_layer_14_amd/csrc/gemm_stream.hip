@@ -26,7 +26,9 @@ constexpr int G2_WAVES = 4;           // mode 1: waves per block (independent it
 
 MOE_DEV i32x4 nt_ld16(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p)); }
 
-MOE_DEV int slab_store_pos(int row, int ch) { return row * (SK * 2) + ((ch ^ (row & 7)) << 4); }
+// 16 rows of 16 chunks: chunk c of row r at position c ^ r, so the 16 rows of one MFMA
+// fragment read (one chunk each) hit 16 distinct positions.
+MOE_DEV int slab_store_pos(int row, int ch) { return row * (SK * 2) + ((ch ^ row) << 4); }
 
 // Per-wave streaming state for one weight matrix slice: 16 rows starting at `w`, row stride `ld`.
 struct SlabStream {

@@ -8,7 +8,7 @@
 // (mode 0: 64 rows of W1 and the same 64 rows of W3, so each wave holds the gate and up
 // accumulators of the same 32 h-columns), k-stage 64. Each stage is loaded from global
 // memory into registers while the previous one is multiplied out of LDS. LDS rows are
-// 128 bytes with their 16-byte chunks XOR-swizzled by (row % 8), so both the stores and
+// 128 bytes with their 16-byte chunks XOR-swizzled by row (swz), so both the stores and
 // the MFMA fragment reads are free of bank conflicts.
 //
 // Work items are (expert, n-tile, m-tile) with the m-tiles of one weight tile adjacent,
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256, kWideBlocksPerCU) void gemm_wide_bf16(
   for (int j = slot; j < chunk; j += per_xcd) {
     const int item = xcd * chunk + j;
     if (item >= items) break;
-    const WideItem it = wide_item(item, tiles, meta, offsets, T, E, per_r, per_s);
+    const WideItem it = wide_item(item, tiles, meta[2], offsets, T, E, per_r, per_s);
     const Tile tl = it.tl;
     const bool sh = it.shared;
     const int K = MODE == 0 ? D : (sh ? S : I);
@@ -163,6 +163,7 @@ __global__ __launch_bounds__(256, kWideBlocksPerCU) void gemm_wide_bf16(
 bool wide_ok(const Dims& d) { return d.dtype == 1 && d.D % 128 == 0 && d.I % 64 == 0 && d.S % 64 == 0; }
 
 hipError_t launch_wide_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s) {
+  if (ring_ok(d)) return launch_ring_bf16(d, w, a, s);
   MOE_LAUNCH(gemm_wide_bf16<0>, dim3(kWideGrid), dim3(256), 0, s, (const bf16_t*)a.x, nullptr, nullptr, a.row_token,
              a.offsets, a.tiles_wide, a.meta, (const bf16_t*)w.w1, (const bf16_t*)w.w3, (const bf16_t*)w.ws1,
              (const bf16_t*)w.ws3, (bf16_t*)a.h_routed, (bf16_t*)a.h_shared, (int)d.T, d.D, d.I, d.S, d.E);

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(MODE == 0 ? 512 : 256, 2) void gemm_wide_fp8(
   for (int j = slot; j < chunk; j += per_xcd) {
     const int item = xcd * chunk + j;
     if (item >= items) break;
-    const WideItem it = wide_item(item, tiles, meta, offsets, T, E, per_r, per_s);
+    const WideItem it = wide_item(item, tiles, meta[2], offsets, T, E, per_r, per_s);
     const Tile tl = it.tl;
     const bool sh = it.shared;
     const int K = MODE == 0 ? D : (sh ? S : I);

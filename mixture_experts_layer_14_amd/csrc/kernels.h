@@ -27,12 +27,14 @@ struct Span {
 // Rows per M-tile of the tile lists the dispatch writes.
 constexpr int kSkinnyBM = 16;
 constexpr int kWideBM = 128;
+constexpr int kWideBM2 = 256;
 constexpr int kDispatchTB = 256;  // tokens per dispatch block
 
 // meta[] written by dispatch_scan (int32):
 //   [0] routed tiles (BM 16)   [1] all tiles (BM 16)
 //   [2] routed tiles (BM 128)  [3] all tiles (BM 128)
 //   [4] experts with tokens
+//   [5] routed tiles (BM 256)  [6] all tiles (BM 256)
 constexpr int kMetaInts = 8;
 
 struct Dims {
@@ -53,7 +55,7 @@ hipError_t launch_router_select(const Dims& d, const double* zpart, int nsplit, 
 int dispatch_blocks(int64_t T);
 hipError_t launch_dispatch(const Dims& d, const int32_t* idx, int32_t* blk, int32_t* counts, int32_t* offsets,
                            int32_t* row_token, int32_t* row_of, int32_t* meta, Tile* tiles_skinny,
-                           Tile* tiles_wide, hipStream_t s);
+                           Tile* tiles_wide, Tile* tiles_wide2, hipStream_t s);
 int64_t max_tiles(const Dims& d, int bm);
 
 // ---- fp8 activation quantisation (x -> e4m3 + per 1x128 scales)
@@ -71,7 +73,8 @@ struct Act {
   const int32_t* offsets;   // [E + 1]
   const int32_t* meta;
   const Tile* tiles_skinny;
-  const Tile* tiles_wide;
+  const Tile* tiles_wide;    // 128-row M-tiles
+  const Tile* tiles_wide2;   // 256-row M-tiles
   void* h_routed;           // [R, I]
   void* h_shared;           // [T, S]
   float* h_scale;           // fp8: [R, I/128]
@@ -87,6 +90,9 @@ int persistent_grid(const void* kernel, int threads, size_t dyn_lds = 0);
 // 128-row LDS-tiled fp8 kernels with 128-k scale promotion (prefill-sized batches)
 bool wide_fp8_ok(const Dims& d);
 hipError_t launch_wide_fp8(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
+// 256-row bf16 kernels fed by a direct-to-LDS 3-stage ring (dim % 128, inter % 64)
+bool ring_ok(const Dims& d);
+hipError_t launch_ring_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
 // 128-row LDS-tiled bf16 kernels (prefill-sized batches)
 bool wide_ok(const Dims& d);
 hipError_t launch_wide_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
@@ -96,8 +102,12 @@ hipError_t launch_combine(const Dims& d, const int32_t* idx, const float* w, con
                           const void* o_routed, const void* o_shared, void* out, hipStream_t s);
 
 // ---- device helpers shared by the 128-row (wide) kernels
-// LDS tile rows are 128 bytes; 16-byte chunks are XOR-swizzled by (row % 8).
-MOE_DEV int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// LDS tile rows are 128 bytes (8 chunks of 16 bytes). Chunk c of row r sits at position
+// c ^ f(r), f(r) = (r ^ (r >> 3)) & 7: any 8 consecutive rows, and the even and the odd rows
+// of any 16 consecutive rows, use 8 distinct positions, so a 16-byte-per-lane fragment read
+// of one chunk over consecutive rows is free of bank conflicts.
+MOE_DEV int swz_key(int row) { return (row ^ (row >> 3)) & 7; }
+MOE_DEV int swz(int row, int chunk) { return row * 128 + ((chunk ^ swz_key(row)) << 4); }
 
 struct WideItem {
   Tile tl;
@@ -106,28 +116,28 @@ struct WideItem {
 };
 
 // item -> (tile, n-tile): routed items first (per_r n-tiles per expert), then the shared
-// expert's (per_s). Within an expert: n-tile major, m-tile minor.
-MOE_DEV WideItem wide_item(int item, const Tile* __restrict__ tiles, const int32_t* __restrict__ meta,
-                           const int32_t* __restrict__ offsets, int T, int E, int per_r, int per_s) {
-  const int nr = meta[2], na = meta[3];
-  WideItem w;
+// expert's (per_s). Within an expert the m-tiles of one n-tile are adjacent, so blocks that
+// run together on one XCD share weight tiles (and, across the window, activation tiles) in L2.
+template <int BM = kWideBM>
+MOE_DEV WideItem wide_item(int item, const Tile* __restrict__ tiles, int nr, const int32_t* __restrict__ offsets,
+                           int T, int E, int per_r, int per_s) {
   int per = per_r, base_tiles = 0, local_item = item;
   if (item >= nr * per_r) {
     per = per_s;
     base_tiles = nr;
     local_item = item - nr * per_r;
   }
-  const int q = base_tiles + local_item / per;  // a tile of the right expert
-  const Tile probe = tiles[q];
+  // the tile with index item / per belongs to the right expert: each expert owns
+  // (its m-tiles) x per consecutive items
+  const Tile probe = tiles[base_tiles + local_item / per];
   const int first = probe.first;
-  const int e = probe.expert;
-  const int rows = e == E ? T : offsets[e + 1] - offsets[e];
-  const int mt = (rows + kWideBM - 1) / kWideBM;
-  const int local = item - (first - base_tiles) * per - (base_tiles ? nr * per_r : 0);
+  const int rows = probe.expert == E ? T : offsets[probe.expert + 1] - offsets[probe.expert];
+  const int mt = (rows + BM - 1) / BM;
+  const int local = local_item - (first - base_tiles) * per;
+  WideItem w;
   w.nt = local / mt;
   w.tl = tiles[first + local % mt];
-  w.shared = e == E;
-  (void)na;
+  w.shared = probe.expert == E;
   return w;
 }
 
