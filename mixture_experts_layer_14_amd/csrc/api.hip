@@ -155,22 +155,23 @@ void drop_spans() {
 }  // namespace
 
 namespace moe {
-int persistent_grid(const void* kernel, int threads, size_t dyn_lds) {
+int persistent_grid(const void* kernel, int threads, size_t dyn_lds, int max_per_cu) {
   static std::mutex mu;
-  static std::map<std::pair<int, const void*>, int> cache;
+  static std::map<std::pair<int, const void*>, std::pair<int, int>> cache;  // (blocks per CU, CUs)
   int dev = 0;
   (void)hipGetDevice(&dev);
   std::lock_guard<std::mutex> lk(mu);
   auto key = std::make_pair(dev, kernel);
   auto it = cache.find(key);
-  if (it != cache.end()) return it->second;
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn_lds) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-  const int g = per_cu * cus;
-  cache[key] = g;
-  return g;
+  if (it == cache.end()) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn_lds) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    it = cache.emplace(key, std::make_pair(per_cu, cus)).first;
+  }
+  const int per_cu = max_per_cu > 0 ? std::min(max_per_cu, it->second.first) : it->second.first;
+  return per_cu * it->second.second;
 }
 
 void span_begin(const char* name, hipStream_t s) {

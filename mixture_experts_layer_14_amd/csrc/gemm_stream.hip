@@ -9,40 +9,51 @@
 // Weights stream through a wave-private LDS slab of 16 rows x 128 k: one wave instruction
 // reads 4 rows x 256 contiguous bytes with nontemporal loads (the pattern HBM serves best),
 // the slab is stored with 16-byte chunks XOR-swizzled by row and read back in MFMA B layout
-// (lane: row = lane % 16, k-chunk 4 s + lane / 16 for 16x16x32 step s). The next slab's loads
-// are in flight while the current one is multiplied. A fragments (x or h rows, a few KB,
-// L2-resident) use the same k mapping.
+// (lane: row = lane % 16, k-chunk 4 s + lane / 16 for 16x16x32 step s). Two slabs per wave are
+// in flight while the current one is multiplied, across item boundaries. A fragments (x or h
+// rows, a few KB, L2-resident) use the same k mapping.
 //
 // Mode 0 splits K = dim over the 8 waves of a 512-thread block and reduces the partial
-// accumulators through LDS in wave order; mode 1 gives each wave a whole 16-column item.
+// accumulators through LDS in wave order; mode 1 gives each wave whole 16-column items.
 #include "kernels.h"
 
 namespace moe {
 
 constexpr int SK = 128;               // k per slab
 constexpr int SLAB = 16 * SK * 2;     // bytes per slab (16 rows)
-constexpr int G1_WAVES = 8;           // mode 0: waves per block (K split)
-constexpr int G2_WAVES = 4;           // mode 1: waves per block (independent items)
-
-MOE_DEV i32x4 nt_ld16(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p)); }
 
 // 16 rows of 16 chunks: chunk c of row r at position c ^ r, so the 16 rows of one MFMA
 // fragment read (one chunk each) hit 16 distinct positions.
 MOE_DEV int slab_store_pos(int row, int ch) { return row * (SK * 2) + ((ch ^ row) << 4); }
 
-// Per-wave streaming state for one weight matrix slice: 16 rows starting at `w`, row stride `ld`.
+// Per-wave streaming state for one weight matrix slice: 16 rows of `ldb` bytes, addressed through
+// a buffer resource (base and byte range in scalar registers), so each lane needs a single 32-bit
+// offset register and the row steps go into the scalar offset. Offsets at or past the range read
+// as zero.
+constexpr int kBufOob = 0x7fffffff;
+constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
+
 struct SlabStream {
-  const bf16_t* w;
-  int ld;
+  __amdgpu_buffer_rsrc_t rs;
+  int ldb;
 };
 
-// Load slab k0 of one matrix: instruction i covers rows 4i + lane/16, chunk lane % 16.
-MOE_DEV void slab_load(i32x4 v[4], const SlabStream& st, int k0, int K, int lane) {
+MOE_DEV SlabStream slab_stream(const bf16_t* rows, int ld) {
+  return {__builtin_amdgcn_make_buffer_rsrc((void*)rows, (short)0, 16 * ld * 2, kBufFlags), ld * 2};
+}
+
+// Load slab k0 of one matrix, nontemporal: instruction i covers rows 4i + lane/16, chunk lane % 16.
+// Lanes past K (a ragged last slab), and every lane when `live` is false, take an out-of-range
+// offset and read zeros without touching memory; the instructions are issued either way, so
+// every step issues the same loads (this keeps the compiler's load-count waits exact).
+MOE_DEV void slab_load(i32x4 v[4], const SlabStream& st, int k0, int K, bool live, int lane) {
   const int q = lane >> 4, c = lane & 15;
   const int k = k0 + c * 8;
-  const i32x4 zero = {0, 0, 0, 0};
+  const int off = (live && k < K) ? q * st.ldb + k * 2 : kBufOob;
+  const int row4 = __builtin_amdgcn_readfirstlane(4 * st.ldb);  // uniform: keep it in a scalar register
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = k < K ? nt_ld16(st.w + (size_t)(4 * i + q) * st.ld + k) : zero;
+  for (int i = 0; i < 4; ++i)
+    v[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(st.rs, off, i * row4, 2));
 }
 
 MOE_DEV void slab_store(char* lds, const i32x4 v[4], int lane) {
@@ -56,95 +67,122 @@ MOE_DEV i32x4 slab_frag(const char* lds, int s, int lane) {
   return *reinterpret_cast<const i32x4*>(lds + slab_store_pos(r, 4 * s + q));
 }
 
-// A fragments of slab k0: lane (row r, q) takes k = k0 + 32 s + 8 q .. + 7 for step s.
-MOE_DEV void a_load(i32x4 a[4], const bf16_t* arow, bool valid, int k0, int K, int lane) {
+// Sixteen zero bytes that A-fragment lanes past K read instead of masking after the load.
+__device__ __attribute__((aligned(16))) const bf16_t kZeroChunk[8] = {};
+
+// A fragments of slab k0: lane (row r, q) takes k = k0 + 32 s + 8 q .. + 7 for step s; lanes
+// past K read kZeroChunk. `arow` is always a readable row: rows past the tile's end read a real
+// row whose products land only in output rows that are never stored (MFMA rows are
+// independent), so they need no masking.
+MOE_DEV void a_load(i32x4 a[4], const bf16_t* arow, int k0, int K, int lane) {
+  typedef const __attribute__((address_space(1))) i32x4* global_i32x4;  // a global load, not a flat one
   const int q = lane >> 4;
-  const i32x4 zero = {0, 0, 0, 0};
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int k = k0 + 32 * s + 8 * q;
-    a[s] = (valid && k < K) ? ld16(arow + k) : zero;
+    a[s] = *(global_i32x4)(k < K ? arow + k : kZeroChunk);
   }
 }
 
-// One wave's pass over k-range [kb, ke) (multiples of SK except a final ragged end):
-// accumulates acc[m] += A * W_m^T for NM matrices.
+// Multiply one landed slab (already in `lds`, NM matrices) with A fragments a: acc[m] += A W_m^T
+// over k0 .. min(k0 + SK, K).
 template <int NM>
-MOE_DEV void stream_range(f32x4 acc[NM], const SlabStream st[NM], const bf16_t* arow, bool avalid, int kb, int ke,
-                          int K, char* lds /* NM slabs */, int lane) {
-  if (kb >= ke) return;
-  i32x4 v[NM][4], a[4], an[4];
+MOE_DEV void slab_mma(f32x4 acc[NM], const i32x4 a[4], const char* lds, int k0, int K, int lane) {
+  const int steps = min(4, (K - k0) >> 5);
 #pragma unroll
-  for (int m = 0; m < NM; ++m) slab_load(v[m], st[m], kb, ke, lane);
-  a_load(a, arow, avalid, kb, ke, lane);
-  for (int k0 = kb; k0 < ke; k0 += SK) {
+  for (int s = 0; s < 4; ++s) {
+    if (s < steps) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m) slab_store(lds + m * SLAB, v[m], lane);
-    const bool more = k0 + SK < ke;
-    if (more) {
-#pragma unroll
-      for (int m = 0; m < NM; ++m) slab_load(v[m], st[m], k0 + SK, ke, lane);
-      a_load(an, arow, avalid, k0 + SK, ke, lane);
-    }
-    const int steps = min(4, (ke - k0) >> 5);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < steps) {
-#pragma unroll
-        for (int m = 0; m < NM; ++m) acc[m] = mfma_bf16_16x16x32(a[s], slab_frag(lds + m * SLAB, s, lane), acc[m]);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) a[s] = an[s];
+      for (int m = 0; m < NM; ++m) acc[m] = mfma_bf16_16x16x32(a[s], slab_frag(lds + m * SLAB, s, lane), acc[m]);
     }
   }
-  (void)K;
 }
 
+// Both kernels run each wave through a flat sequence of steps (one slab of one item each) with
+// two weight slabs in flight: step n multiplies the slab held in register set n % 2, after storing
+// it to the wave's LDS slab and requesting slab n + 2 into the same registers. The request cursor
+// runs on into the next item, so the weight stream does not drain at item boundaries.
+//
+// Vector-memory loads complete in issue order, so waiting for any load also waits for every
+// older one. A fragments of step n + 1 (an L2 hit) are therefore requested before slab n + 2, into
+// the second of two A register sets, and the step-n MFMAs wait only for loads issued before
+// slab n + 1: two slabs really stay in flight.
+MOE_DEV void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0): this wave's LDS traffic done
+  __builtin_amdgcn_s_barrier();                                // loads in flight stay in flight
+}
+
+// mode 0: 8 waves per block split K; two slab sets, two A sets and the accumulators take ~146
+// VGPRs, so one block (2 waves per SIMD) is resident per CU: 128 KB of weights in flight per CU.
+// (4-wave blocks at 3 per CU, or 8-wave blocks held to 128 VGPRs with spills, measured slower.)
+constexpr int G1_WAVES = 8;
+// mode 1: 4 waves per block, each with its own items; ~100 registers, 4 blocks per CU (the rate
+// did not change between 2 and 5 blocks per CU).
+constexpr int G2_WAVES = 4;
+
 // ---------------------------------------------------------------------------
-// mode 0: gate/up + SwiGLU. Block = 8 waves = one item (16 rows x 16 h-columns); wave w
-// streams the w-th contiguous eighth of D (whole slabs). After the pass each wave's slab
-// buffer holds its partial accumulators for the in-order reduction by wave 0.
+// mode 0: gate/up + SwiGLU. Item = 16 rows x 16 h-columns; wave w of a block streams the w-th
+// contiguous share of D (whole slabs) of every item of the block. At an item's end each wave parks
+// its partial accumulators in its slab area and wave 0 reduces them in wave order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64 * G1_WAVES, 4) void gemm1_stream_bf16(
+struct G1Info {  // wave-uniform
+  Tile tl;
+  bool sh;
+  int nt;
+  SlabStream st[2];
+};
+
+MOE_DEV G1Info g1_info(int item, const Tile* tiles, int nr, int per_r, int per_s, const bf16_t* w1,
+                       const bf16_t* w3, const bf16_t* ws1, const bf16_t* ws3, int D, int I, int E) {
+  G1Info g;
+  int ti;
+  if (item < nr * per_r) {
+    ti = item / per_r;
+    g.nt = item % per_r;
+  } else {
+    ti = nr + (item - nr * per_r) / per_s;
+    g.nt = (item - nr * per_r) % per_s;
+  }
+  g.tl = tiles[ti];
+  g.sh = g.tl.expert == E;
+  const size_t eoff = g.sh ? 0 : (size_t)g.tl.expert * I * D;
+  g.st[0] = slab_stream((g.sh ? ws1 : w1 + eoff) + (size_t)g.nt * 16 * D, D);
+  g.st[1] = slab_stream((g.sh ? ws3 : w3 + eoff) + (size_t)g.nt * 16 * D, D);
+  return g;
+}
+
+// x row of this lane's tile row (rows past the tile's end read token 0)
+MOE_DEV const bf16_t* g1_arow(const G1Info& g, const bf16_t* x, const int32_t* row_token, int D, int r) {
+  int tok = 0;
+  if (r < g.tl.nrows) tok = g.sh ? g.tl.row0 + r : row_token[g.tl.row0 + r];
+  return x + (size_t)tok * D;
+}
+
+__global__ __launch_bounds__(64 * G1_WAVES, 2) void gemm1_stream_bf16(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ row_token, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ meta, const bf16_t* __restrict__ w1, const bf16_t* __restrict__ w3,
     const bf16_t* __restrict__ ws1, const bf16_t* __restrict__ ws3, bf16_t* __restrict__ h_routed,
     bf16_t* __restrict__ h_shared, int D, int I, int S, int E) {
   __shared__ __attribute__((aligned(16))) char lds[G1_WAVES][2 * SLAB];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, q = lane >> 4;
   const int per_r = I / 16, per_s = S / 16;
   const int nr = meta[0];
   const int items = nr * per_r + (meta[1] - nr) * per_s;
-  // contiguous k-range of this wave, in whole slabs
+  // contiguous k-range of this wave, in whole slabs (empty when D has fewer slabs than waves)
   const int nslab = (D + SK - 1) / SK;
   const int kb = (nslab * wave / G1_WAVES) * SK;
   const int ke = min(D, (nslab * (wave + 1) / G1_WAVES) * SK);
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    int ti, nt;
-    if (item < nr * per_r) {
-      ti = item / per_r;
-      nt = item % per_r;
-    } else {
-      ti = nr + (item - nr * per_r) / per_s;
-      nt = (item - nr * per_r) % per_s;
-    }
-    const Tile tl = tiles[ti];
-    const bool sh = tl.expert == E;
-    const size_t eoff = sh ? 0 : (size_t)tl.expert * I * D;
-    SlabStream st[2] = {{(sh ? ws1 : w1 + eoff) + (size_t)nt * 16 * D, D},
-                        {(sh ? ws3 : w3 + eoff) + (size_t)nt * 16 * D, D}};
-    const bool av = r < tl.nrows;
-    int tok = 0;
-    if (av) tok = sh ? tl.row0 + r : row_token[tl.row0 + r];
-    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    stream_range<2>(acc, st, x + (size_t)tok * D, av, kb, ke, D, lds[wave], lane);
-    f32x4* red = reinterpret_cast<f32x4*>(lds[wave]);  // this wave is done with its slabs
+  int item = blockIdx.x;
+  if (item >= items) return;
+  f32x4* red = reinterpret_cast<f32x4*>(lds[wave]);
+  auto info_at = [&](int it) { return g1_info(it, tiles, nr, per_r, per_s, w1, w3, ws1, ws3, D, I, E); };
+
+  // At an item's end: partials to LDS, wave 0 reduces in wave order, applies SwiGLU and stores.
+  auto finish = [&](const G1Info& c, const f32x4 acc[2]) {
     red[lane] = acc[0];
     red[64 + lane] = acc[1];
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
       f32x4 g = acc[0], u = acc[1];
 #pragma unroll
@@ -156,44 +194,204 @@ __global__ __launch_bounds__(64 * G1_WAVES, 4) void gemm1_stream_bf16(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = q * 4 + i;
-        if (row < tl.nrows) {
-          bf16_t* dst = sh ? h_shared + (size_t)(tl.row0 + row) * S : h_routed + (size_t)(tl.row0 + row) * I;
-          dst[nt * 16 + r] = f32_to_bf16(silu_mul(g[i], u[i]));
+        if (row < c.tl.nrows) {
+          bf16_t* dst = c.sh ? h_shared + (size_t)(c.tl.row0 + row) * S : h_routed + (size_t)(c.tl.row0 + row) * I;
+          dst[c.nt * 16 + r] = f32_to_bf16(silu_mul(g[i], u[i]));
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
+  };
+
+  if (kb >= ke) {  // no slabs for this wave: take part in every item's reduction with zeros
+    const f32x4 zero[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (; item < items; item += gridDim.x) finish(info_at(item), zero);
+    return;
+  }
+
+  // request cursor (slab n + 2)
+  int l_item = item, l_k0 = kb;
+  G1Info l = info_at(l_item);
+  auto request = [&](i32x4 v[2][4]) {  // past the block's last item: zeros, no traffic
+    const bool live = l_item < items;
+    slab_load(v[0], l.st[0], l_k0, ke, live, lane);
+    slab_load(v[1], l.st[1], l_k0, ke, live, lane);
+    if (!live) return;
+    l_k0 += SK;
+    if (l_k0 >= ke) {
+      l_item += gridDim.x;
+      l_k0 = kb;
+      if (l_item < items) l = info_at(l_item);
+    }
+  };
+  // A cursor (step n + 1)
+  int p_item = item, p_k0 = kb;
+  const bf16_t* p_arow = g1_arow(l, x, row_token, D, r);
+  auto a_next = [&](i32x4 a[4]) {
+    const bool live = p_item < items;
+    a_load(a, p_arow, p_k0, live ? ke : 0, lane);
+    if (!live) return;
+    p_k0 += SK;
+    if (p_k0 >= ke) {
+      p_item += gridDim.x;
+      p_k0 = kb;
+      if (p_item < items) p_arow = g1_arow(info_at(p_item), x, row_token, D, r);
+    }
+  };
+  i32x4 v0[2][4], v1[2][4], a0[4], a1[4];
+  // same issue order as the steady state (A of a step goes out between the two slabs ahead)
+  request(v0);
+  a_next(a0);
+  request(v1);
+  // compute cursor (step n)
+  G1Info c = info_at(item);
+  int c_k0 = kb;
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // One step on register sets v / a (A of the following step goes to an). Every step issues the
+  // same loads, and the loop has a single exit after the second step of a trip: otherwise the
+  // compiler merges a load-free or early-exit path into the loop head and waits there for every
+  // load in flight. A step after the last item only issues (empty) loads.
+  bool done = false;
+  auto step = [&](i32x4 v[2][4], const i32x4 a[4], i32x4 an[4]) {
+    slab_store(lds[wave], v[0], lane);
+    slab_store(lds[wave] + SLAB, v[1], lane);
+    a_next(an);
+    request(v);
+    if (done) return;
+    slab_mma<2>(acc, a, lds[wave], c_k0, ke, lane);
+    c_k0 += SK;
+    if (c_k0 >= ke) {
+      finish(c, acc);
+      acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      item += gridDim.x;
+      done = item >= items;
+      if (!done) c = info_at(item);
+      c_k0 = kb;
+    }
+  };
+  for (;;) {  // two steps per trip so the register sets alternate statically
+    step(v0, a0, a1);
+    step(v1, a1, a0);
+    if (done) return;
   }
 }
 
 // ---------------------------------------------------------------------------
-// mode 1: down projection. Each wave owns whole items of 16 rows x 16 output columns.
+// mode 1: down projection. Each wave owns whole items of 16 rows x 16 output columns and walks
+// its items as one continuous weight stream.
 // ---------------------------------------------------------------------------
+struct G2Info {  // wave-uniform
+  Tile tl;
+  bool sh;
+  int nt, K, rot;
+  SlabStream st;
+};
+
+// Physical k of logical k offset k0 of item g. Items start their k walk at different slabs: with
+// every wave at the same offset of 4 KB-strided rows, concurrent requests bunch on a few HBM
+// channels (measured: 6.4 TB/s in step, 6.7 TB/s staggered).
+MOE_DEV int g2_k(const G2Info& g, int k0) {
+  const int k = k0 + g.rot;
+  return k >= g.K ? k - g.K : k;
+}
+
+MOE_DEV G2Info g2_info(int item, const Tile* tiles, int per, const bf16_t* w2, const bf16_t* ws2, int D, int I,
+                       int S, int E) {
+  G2Info g;
+  const int ti = item / per;
+  g.nt = item % per;
+  g.tl = tiles[ti];
+  g.sh = g.tl.expert == E;
+  g.K = g.sh ? S : I;
+  g.st = slab_stream((g.sh ? ws2 : w2 + (size_t)g.tl.expert * D * I) + (size_t)g.nt * 16 * g.K, g.K);
+  g.rot = g.K % SK == 0 ? ((g.nt * 5 + g.tl.expert * 3) % (g.K / SK)) * SK : 0;
+  return g;
+}
+
+// h row of this lane's tile row (rows past the tile's end read the tile's row 0)
+MOE_DEV const bf16_t* g2_arow(const G2Info& g, const bf16_t* h_routed, const bf16_t* h_shared, int r) {
+  const bf16_t* A = g.sh ? h_shared : h_routed;
+  return A + (size_t)(g.tl.row0 + (r < g.tl.nrows ? r : 0)) * g.K;
+}
+
 __global__ __launch_bounds__(64 * G2_WAVES) void gemm2_stream_bf16(
     const bf16_t* __restrict__ h_routed, const bf16_t* __restrict__ h_shared, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ meta, const bf16_t* __restrict__ w2, const bf16_t* __restrict__ ws2,
     bf16_t* __restrict__ o_routed, bf16_t* __restrict__ o_shared, int D, int I, int S, int E) {
   __shared__ __attribute__((aligned(16))) char lds[G2_WAVES][SLAB];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, q = lane >> 4;
   const int per = D / 16;
   const int items = meta[1] * per;
-  for (int item = blockIdx.x * G2_WAVES + wave; item < items; item += gridDim.x * G2_WAVES) {
-    const int ti = item / per, nt = item % per;
-    const Tile tl = tiles[ti];
-    const bool sh = tl.expert == E;
-    const int K = sh ? S : I;
-    const bf16_t* A = sh ? h_shared + (size_t)tl.row0 * S : h_routed + (size_t)tl.row0 * I;
-    SlabStream st[1] = {{(sh ? ws2 : w2 + (size_t)tl.expert * D * I) + (size_t)nt * 16 * K, K}};
-    const bool av = r < tl.nrows;
-    f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
-    stream_range<1>(acc, st, A + (size_t)(av ? r : 0) * K, av, 0, K, K, lds[wave], lane);
-    bf16_t* O = sh ? o_shared : o_routed;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = q * 4 + i;
-      if (row < tl.nrows) O[(size_t)(tl.row0 + row) * D + nt * 16 + r] = f32_to_bf16(acc[0][i]);
+  const int stride = gridDim.x * G2_WAVES;
+  int item = blockIdx.x * G2_WAVES + wave;
+  if (item >= items) return;
+  auto info_at = [&](int it) { return g2_info(it, tiles, per, w2, ws2, D, I, S, E); };
+
+  int l_item = item, l_k0 = 0;
+  G2Info l = info_at(l_item);
+  auto request = [&](i32x4 v[4]) {
+    const bool live = l_item < items;
+    slab_load(v, l.st, g2_k(l, l_k0), l.K, live, lane);
+    if (!live) return;
+    l_k0 += SK;
+    if (l_k0 >= l.K) {
+      l_item += stride;
+      l_k0 = 0;
+      if (l_item < items) l = info_at(l_item);
     }
+  };
+  int p_item = item, p_k0 = 0;
+  G2Info p = l;
+  const bf16_t* p_arow = g2_arow(p, h_routed, h_shared, r);
+  auto a_next = [&](i32x4 a[4]) {
+    const bool live = p_item < items;
+    a_load(a, p_arow, g2_k(p, p_k0), live ? p.K : 0, lane);
+    if (!live) return;
+    p_k0 += SK;
+    if (p_k0 >= p.K) {
+      p_item += stride;
+      p_k0 = 0;
+      if (p_item < items) {
+        p = info_at(p_item);
+        p_arow = g2_arow(p, h_routed, h_shared, r);
+      }
+    }
+  };
+  i32x4 v0[4], v1[4], a0[4], a1[4];
+  // same issue order as the steady state (A of a step goes out between the two slabs ahead)
+  request(v0);
+  a_next(a0);
+  request(v1);
+  G2Info c = info_at(item);
+  int c_k0 = 0;
+  f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+  bool done = false;  // same step and loop shape as mode 0
+  auto step = [&](i32x4 v[4], const i32x4 a[4], i32x4 an[4]) {
+    slab_store(lds[wave], v, lane);
+    a_next(an);
+    request(v);
+    if (done) return;
+    slab_mma<1>(acc, a, lds[wave], g2_k(c, c_k0), c.K, lane);
+    c_k0 += SK;
+    if (c_k0 >= c.K) {
+      bf16_t* O = c.sh ? o_shared : o_routed;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = q * 4 + i;
+        if (row < c.tl.nrows) O[(size_t)(c.tl.row0 + row) * D + c.nt * 16 + r] = f32_to_bf16(acc[0][i]);
+      }
+      acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      item += stride;
+      done = item >= items;
+      if (!done) c = info_at(item);
+      c_k0 = 0;
+    }
+  };
+  for (;;) {
+    step(v0, a0, a1);
+    step(v1, a1, a0);
+    if (done) return;
   }
 }
 

@@ -85,8 +85,9 @@ struct Act {
 hipError_t launch_experts(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
 // 16-row weight-streaming bf16 kernels (decode-sized batches)
 hipError_t launch_stream_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
-// Blocks of `kernel` that fit on the current device at once (occupancy x CUs), cached.
-int persistent_grid(const void* kernel, int threads, size_t dyn_lds = 0);
+// Blocks of `kernel` that fit on the current device at once (occupancy x CUs, the occupancy capped
+// at max_per_cu when that is positive), cached per device and kernel.
+int persistent_grid(const void* kernel, int threads, size_t dyn_lds = 0, int max_per_cu = 0);
 // 128-row LDS-tiled fp8 kernels with 128-k scale promotion (prefill-sized batches)
 bool wide_fp8_ok(const Dims& d);
 hipError_t launch_wide_fp8(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
