@@ -6,8 +6,10 @@ over one batch of synthetic tokens already resident in HBM. The default workload
 block at decode shape: 16 tokens, dim 7168, 256 routed + 1 shared expert (inter 2048), bf16.
 
 Prints one JSON line: tokens/s, ms per step, the dominant kernel's roofline (algorithmic bytes or
-flops per launch over its average HIP-event-timed duration) and the CPU oracle timed on a bounded
-sample of the same workload.
+flops per launch over its average duration, from HIP events around that kernel's launches inside
+the timed steps) and the CPU oracle timed on a bounded sample of the same workload. A pass of the
+same number of untimed steps before the timed ones, with events around every launch, gives the
+per-kernel breakdown (`kernels_ms`) and picks the dominant kernel.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -133,7 +135,21 @@ def main():
     counts = blk.ws_view(T, "counts", torch.int32, shape.n_experts).cpu().numpy()
     touched, units = kernel_units(shape, counts)
 
+    # Per-kernel breakdown: K untimed steps with HIP events around every launch (they add a few
+    # microseconds per launch, so the timed steps below keep them on the dominant kernel only).
+    print(f"[bench] per-kernel pass, {args.steps} steps", file=sys.stderr, flush=True)
+    moe.timing_filter(None)
+    moe.timing_enable(True)
+    for _ in range(args.steps):
+        blk.forward(tens.x, out)
+    torch.cuda.synchronize()
+    kt = moe.timing_report()
+    moe.timing_enable(False)
+    kernels = {name: (cnt, tot / cnt) for name, (cnt, tot) in kt.items()}
+    dom = max(kernels, key=lambda n: kernels[n][0] * kernels[n][1])
+
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    moe.timing_filter(dom)
     moe.timing_enable(True)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -143,12 +159,11 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    kt = moe.timing_report()
+    kt_dom = moe.timing_report()
     moe.timing_enable(False)
-
-    kernels = {name: (cnt, tot / cnt) for name, (cnt, tot) in kt.items()}
-    dom = max(kernels, key=lambda n: kernels[n][0] * kernels[n][1])
-    dom_ms = kernels[dom][1]
+    moe.timing_filter(None)
+    dom_cnt, dom_tot = kt_dom[dom]
+    dom_ms = dom_tot / dom_cnt
     kind = "gemm1" if ("gemm1" in dom or "<0" in dom) else ("gemm2" if ("gemm2" in dom or "<1" in dom) else None)
     decode_like = T <= 256
     roof = None

@@ -150,6 +150,10 @@ moe_status moe_workspace_layout(const moe_config* cfg, int64_t T, moe_ws_layout*
  * creates HIP events (a host-side allocation), so do it outside code that must not allocate.
  * Errors: MOE_ERR_HIP if events cannot be created. Not thread-safe with concurrent launches. */
 moe_status moe_timing_enable(int on);
+/* Restrict the spans to kernels whose name contains name_part (NULL or "" = every kernel); the
+ * events cost a few microseconds per launch, so a measurement can keep them on the kernel it
+ * studies only. Persists across moe_timing_enable. Always MOE_OK. */
+moe_status moe_timing_filter(const char* name_part);
 /* Waits for the recorded events, then writes one line per kernel name,
  * "<name> <launches> <total milliseconds>\n", into buf (NUL-terminated, truncated to
  * bytes) and clears the records. Returns the number of lines, or a negative moe_status. */

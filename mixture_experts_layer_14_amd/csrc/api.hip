@@ -25,7 +25,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   moe_ws_layout pub;
-  size_t meta, blk, tiles_s, tiles_w, tiles_w2, zpart, z32;
+  size_t meta, blk, tiles_s, tiles_w, tiles_w2, zpart;
   int nsplit;
 };
 
@@ -91,7 +91,6 @@ Layout plan(const moe::Dims& d) {
   L.tiles_w2 = take((size_t)moe::max_tiles(d, moe::kWideBM2) * sizeof(Tile));
   L.nsplit = moe::router_splits(d);
   L.zpart = take((size_t)L.nsplit * d.T * d.E * 8);
-  L.z32 = take((size_t)d.T * d.E * 4);
   L.pub.xq = take(fp8 ? (size_t)d.T * d.D : 0);
   L.pub.x_scale = take(fp8 ? (size_t)d.T * (d.D / 128) * 4 : 0);
   L.pub.h_routed = take((size_t)d.R * d.I * act);
@@ -130,6 +129,7 @@ struct SpanRec {
 };
 std::mutex g_tmu;
 bool g_timing = false;
+std::string g_filter;  // record only kernels whose name contains this ("" = all)
 std::vector<hipEvent_t> g_pool;
 std::vector<SpanRec> g_spans;
 
@@ -174,12 +174,14 @@ int persistent_grid(const void* kernel, int threads, size_t dyn_lds, int max_per
   return per_cu * it->second.second;
 }
 
-void span_begin(const char* name, hipStream_t s) {
-  if (!g_timing) return;
+bool span_begin(const char* name, hipStream_t s) {
+  if (!g_timing) return false;
   std::lock_guard<std::mutex> lk(g_tmu);
+  if (!g_filter.empty() && !strstr(name, g_filter.c_str())) return false;
   SpanRec r{name, take_event(), nullptr};
   if (r.a) (void)hipEventRecord(r.a, s);
   g_spans.push_back(r);
+  return true;
 }
 void span_end(hipStream_t s) {
   if (!g_timing) return;
@@ -203,6 +205,12 @@ moe_status moe_timing_enable(int on) {
     g_pool.push_back(e);
   }
   g_timing = on != 0;
+  return MOE_OK;
+}
+
+moe_status moe_timing_filter(const char* name_part) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_filter = name_part ? name_part : "";
   return MOE_OK;
 }
 
@@ -276,7 +284,7 @@ moe_status moe_route(const moe_config* cfg, const void* w_gate, const float* bia
   double* zpart = at<double>(ws, L.zpart);
   if ((st = hip_status(moe::launch_router_logits(d, x, w_gate, zpart, L.nsplit, s), "router logits")) != MOE_OK)
     return st;
-  return hip_status(moe::launch_router_select(d, zpart, L.nsplit, at<float>(ws, L.z32), bias, cfg->route_scale, idx, w, s),
+  return hip_status(moe::launch_router_select(d, zpart, L.nsplit, bias, cfg->route_scale, idx, w, s),
                     "router select");
 }
 
@@ -331,7 +339,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wts, const void
     return st;
   if ((st = hip_status(moe::launch_router_logits(d, x, wts->w_gate, zpart, L.nsplit, s), "router logits")) != MOE_OK)
     return st;
-  if ((st = hip_status(moe::launch_router_select(d, zpart, L.nsplit, at<float>(ws, L.z32), wts->bias, cfg->route_scale, idx, w, s),
+  if ((st = hip_status(moe::launch_router_select(d, zpart, L.nsplit, wts->bias, cfg->route_scale, idx, w, s),
                        "router select")) != MOE_OK)
     return st;
   if ((st = hip_status(moe::launch_dispatch(d, idx, at<int32_t>(ws, L.blk), at<int32_t>(ws, L.pub.counts), offsets,

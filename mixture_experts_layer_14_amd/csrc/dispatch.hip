@@ -8,6 +8,7 @@
 //   scan:    one workgroup: blk[b][e] -> base row of block b inside expert e,
 //            counts, offsets, and the GEMM tile lists (M-tiles of 16, 128 and 256 rows)
 //   scatter: rebuilds the bitmap; row = base + popcount of earlier tokens' bits
+// Up to 256 tokens (one block) all three run in a single workgroup (dispatch_single).
 #include "kernels.h"
 
 namespace moe {
@@ -107,6 +108,44 @@ __device__ void write_tiles(const int* cnt, const int* off, int E, int T, int bm
   }
 }
 
+// From cnt[E] (LDS): off[0..E] (LDS), counts/offsets, the three tile lists and meta.
+__device__ void publish(const int* cnt, int* off, int E, int T, int32_t* __restrict__ counts,
+                        int32_t* __restrict__ offsets, int32_t* __restrict__ meta, Tile* __restrict__ tiles_s,
+                        Tile* __restrict__ tiles_w, Tile* __restrict__ tiles_w2, int* scratch) {
+  const int per = (E + 255) / 256;
+  int mine = 0;
+  for (int j = 0; j < per; ++j) {
+    int e = threadIdx.x * per + j;
+    if (e < E) mine += cnt[e];
+  }
+  int total;
+  int base = block_exclusive_scan(mine, scratch, &total);
+  int active = 0;
+  for (int j = 0; j < per; ++j) {
+    int e = threadIdx.x * per + j;
+    if (e >= E) break;
+    off[e] = base;
+    base += cnt[e];
+    active += cnt[e] > 0;
+  }
+  if (threadIdx.x == 0) off[E] = total;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    counts[e] = cnt[e];
+    offsets[e] = off[e];
+  }
+  if (threadIdx.x == 0) offsets[E] = off[E];
+  int nact;
+  block_exclusive_scan(active, scratch, &nact);
+  write_tiles(cnt, off, E, T, kSkinnyBM, tiles_s, &meta[0], &meta[1], scratch);
+  __syncthreads();
+  write_tiles(cnt, off, E, T, kWideBM, tiles_w, &meta[2], &meta[3], scratch);
+  __syncthreads();
+  write_tiles(cnt, off, E, T, kWideBM2, tiles_w2, &meta[5], &meta[6], scratch);
+  if (threadIdx.x == 0) meta[4] = nact;
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(256) void dispatch_scan(int32_t* __restrict__ blk, int nblk, int E, int T,
                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ meta, Tile* __restrict__ tiles_s,
@@ -128,44 +167,16 @@ __global__ __launch_bounds__(256) void dispatch_scan(int32_t* __restrict__ blk, 
     cnt[e] = run;
   }
   __syncthreads();
-  int mine = 0;
-  for (int j = 0; j < per; ++j) {
-    int e = threadIdx.x * per + j;
-    if (e < E) mine += cnt[e];
-  }
-  int total;
-  int base = block_exclusive_scan(mine, scratch, &total);
-  int active = 0;
-  for (int j = 0; j < per; ++j) {
-    int e = threadIdx.x * per + j;
-    if (e >= E) break;
-    off[e] = base;
-    base += cnt[e];
-    active += cnt[e] > 0;
-  }
-  if (threadIdx.x == 0) off[E] = total;
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    counts[e] = cnt[e];
-    offsets[e] = off[e];
+  publish(cnt, off, E, T, counts, offsets, meta, tiles_s, tiles_w, tiles_w2, scratch);
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
     for (int b = 0; b < nblk; ++b) blk[(size_t)b * E + e] += off[e];
-  }
-  if (threadIdx.x == 0) offsets[E] = off[E];
-  int nact;
-  block_exclusive_scan(active, scratch, &nact);
-  write_tiles(cnt, off, E, T, kSkinnyBM, tiles_s, &meta[0], &meta[1], scratch);
-  __syncthreads();
-  write_tiles(cnt, off, E, T, kWideBM, tiles_w, &meta[2], &meta[3], scratch);
-  __syncthreads();
-  write_tiles(cnt, off, E, T, kWideBM2, tiles_w2, &meta[5], &meta[6], scratch);
-  if (threadIdx.x == 0) meta[4] = nact;
 }
 
-__global__ __launch_bounds__(TB) void dispatch_scatter(const int32_t* __restrict__ idx, int T, int K, int E,
-                                                       const int32_t* __restrict__ blk,
-                                                       int32_t* __restrict__ row_token, int32_t* __restrict__ row_of) {
-  extern __shared__ unsigned long long bits[];
-  build_bits(bits, idx, T, K, E);
+// Row of token t's k-th choice e: base row of e for this token block + earlier tokens of the
+// block that chose e (popcount of their bits).
+__device__ void scatter_rows(const unsigned long long* bits, const int32_t* __restrict__ idx, int T, int K, int E,
+                             const int* base /* [E], this block */, int32_t* __restrict__ row_token,
+                             int32_t* __restrict__ row_of) {
   int t = blockIdx.x * TB + threadIdx.x;
   if (t >= T) return;
   const int w = threadIdx.x >> 6;
@@ -175,10 +186,40 @@ __global__ __launch_bounds__(TB) void dispatch_scatter(const int32_t* __restrict
     if ((unsigned)e >= (unsigned)E) continue;
     int rank = __popcll(bits[e * WORDS + w] & below);
     for (int ww = 0; ww < w; ++ww) rank += __popcll(bits[e * WORDS + ww]);
-    int row = blk[(size_t)blockIdx.x * E + e] + rank;
+    int row = base[e] + rank;
     row_token[row] = t;
     row_of[(size_t)t * K + k] = row;
   }
+}
+
+// T <= 256: count, scan and scatter in one workgroup.
+__global__ __launch_bounds__(TB) void dispatch_single(const int32_t* __restrict__ idx, int T, int K, int E,
+                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ meta, Tile* __restrict__ tiles_s,
+                                                      Tile* __restrict__ tiles_w, Tile* __restrict__ tiles_w2,
+                                                      int32_t* __restrict__ row_token, int32_t* __restrict__ row_of) {
+  extern __shared__ unsigned long long bits[];
+  __shared__ int cnt[1024];
+  __shared__ int off[1025];
+  __shared__ int scratch[4];
+  build_bits(bits, idx, T, K, E);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < WORDS; ++w) c += __popcll(bits[e * WORDS + w]);
+    cnt[e] = c;
+  }
+  __syncthreads();
+  publish(cnt, off, E, T, counts, offsets, meta, tiles_s, tiles_w, tiles_w2, scratch);
+  scatter_rows(bits, idx, T, K, E, off, row_token, row_of);
+}
+
+__global__ __launch_bounds__(TB) void dispatch_scatter(const int32_t* __restrict__ idx, int T, int K, int E,
+                                                       const int32_t* __restrict__ blk,
+                                                       int32_t* __restrict__ row_token, int32_t* __restrict__ row_of) {
+  extern __shared__ unsigned long long bits[];
+  build_bits(bits, idx, T, K, E);
+  scatter_rows(bits, idx, T, K, E, blk + (size_t)blockIdx.x * E, row_token, row_of);
 }
 
 int dispatch_blocks(int64_t T) { return (int)((T + TB - 1) / TB); }
@@ -190,15 +231,15 @@ hipError_t launch_dispatch(const Dims& d, const int32_t* idx, int32_t* blk, int3
                            Tile* tiles_w2, hipStream_t s) {
   int nblk = dispatch_blocks(d.T);
   size_t lds = (size_t)d.E * WORDS * sizeof(unsigned long long);
-  if (nblk > 0) {
-    MOE_LAUNCH(dispatch_count, dim3(nblk), dim3(TB), lds, s, idx, (int)d.T, d.K, d.E, blk);
+  if (nblk <= 1) {
+    MOE_LAUNCH(dispatch_single, dim3(1), dim3(TB), lds, s, idx, (int)d.T, d.K, d.E, counts, offsets, meta, tiles_s,
+               tiles_w, tiles_w2, row_token, row_of);
+    return hipGetLastError();
   }
-  MOE_LAUNCH(dispatch_scan, dim3(1), dim3(256), 0, s, blk, nblk, d.E, (int)d.T, counts, offsets, meta,
-                     tiles_s, tiles_w, tiles_w2);
-  if (nblk > 0) {
-    MOE_LAUNCH(dispatch_scatter, dim3(nblk), dim3(TB), lds, s, idx, (int)d.T, d.K, d.E, blk, row_token,
-                       row_of);
-  }
+  MOE_LAUNCH(dispatch_count, dim3(nblk), dim3(TB), lds, s, idx, (int)d.T, d.K, d.E, blk);
+  MOE_LAUNCH(dispatch_scan, dim3(1), dim3(256), 0, s, blk, nblk, d.E, (int)d.T, counts, offsets, meta, tiles_s,
+             tiles_w, tiles_w2);
+  MOE_LAUNCH(dispatch_scatter, dim3(nblk), dim3(TB), lds, s, idx, (int)d.T, d.K, d.E, blk, row_token, row_of);
   return hipGetLastError();
 }
 

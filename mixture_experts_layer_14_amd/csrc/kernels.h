@@ -8,14 +8,18 @@
 
 namespace moe {
 
-// Measurement spans: when timing is enabled (moe_timing_enable), each kernel launch is
-// bracketed by HIP events on its stream; otherwise these do nothing.
-void span_begin(const char* name, hipStream_t s);
+// Measurement spans: when timing is enabled (moe_timing_enable), each kernel launch whose name
+// passes the filter (moe_timing_filter) is bracketed by HIP events on its stream; otherwise these
+// do nothing. span_begin returns whether it recorded.
+bool span_begin(const char* name, hipStream_t s);
 void span_end(hipStream_t s);
 struct Span {
   hipStream_t s;
-  Span(const char* name, hipStream_t st) : s(st) { span_begin(name, st); }
-  ~Span() { span_end(s); }
+  bool on;
+  Span(const char* name, hipStream_t st) : s(st), on(span_begin(name, st)) {}
+  ~Span() {
+    if (on) span_end(s);
+  }
 };
 // Launch `kernel` on stream `s` (a variable in scope) inside a measurement span.
 #define MOE_LAUNCH(kernel, ...)                         \
@@ -47,8 +51,8 @@ struct Dims {
 int router_splits(const Dims& d);
 hipError_t launch_router_logits(const Dims& d, const void* x, const void* w_gate, double* zpart, int nsplit,
                                 hipStream_t s);
-// nsplit > 1: a reduce kernel sums the slices into z32 [T, E] first.
-hipError_t launch_router_select(const Dims& d, const double* zpart, int nsplit, float* z32, const float* bias,
+// Sums the nsplit slices of zpart per token in slice order, then scores, groups and selects.
+hipError_t launch_router_select(const Dims& d, const double* zpart, int nsplit, const float* bias,
                                 float route_scale, int32_t* idx, float* w, hipStream_t s);
 
 // ---- dispatch

@@ -15,22 +15,28 @@ namespace moe {
 // fp32, chunk sum rounded once) and the chunks are summed in fp64, so z keeps
 // well under 1e-7 absolute error before its single rounding to fp32. Partial
 // sums over `nsplit` slices of D are written to zpart[split][T][E] (fp64) and
-// added in split order by router_reduce.
+// added in slice order by router_select.
 //
-// Block: 4 waves; wave tile 32 tokens x 32 experts (2 x 2 MFMA tiles); block
-// tile 32 tokens x 128 experts. Grid (T/32, E/128, nsplit).
+// Block: 4 waves on one tile of 32 tokens x 32 experts (2 x 2 MFMA tiles); wave w takes the
+// w-th quarter of the block's slice (whole chunks) and wave 0 adds the four fp64 partial tiles
+// in wave order. Grid (T/32, E/32, nsplit).
 // ---------------------------------------------------------------------------
+constexpr int kMaxSplit = 8;
+
 __global__ __launch_bounds__(256) void router_logits_bf16(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ wg,
                                                           double* __restrict__ zpart, int T, int D, int E,
                                                           int kslice) {
+  __shared__ double red[3][16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, kq = lane >> 4;
   const int t0 = blockIdx.x * 32;
-  const int e0 = blockIdx.y * 128 + wave * 32;
+  const int e0 = blockIdx.y * 32;
   const int split = blockIdx.z;
-  const int kb = split * kslice;
-  const int ke = min(D, kb + kslice);
+  const int sb = split * kslice;
+  const int nch = max(0, min(D, sb + kslice) - sb) / 32;
+  const int kb = sb + (nch * wave / 4) * 32;
+  const int ke = sb + (nch * (wave + 1) / 4) * 32;
 
   const bf16_t* ap[2];
   bool av[2];
@@ -58,12 +64,10 @@ __global__ __launch_bounds__(256) void router_logits_bf16(const bf16_t* __restri
 
   const i32x4 zero = {0, 0, 0, 0};
   const f32x4 fz = {0.f, 0.f, 0.f, 0.f};
-  for (int k = kb; k < ke; k += 32) {
-    i32x4 a[2], b[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) a[m] = av[m] ? ld16(ap[m] + k) : zero;
-#pragma unroll
-    for (int n = 0; n < 2; ++n) b[n] = bv[n] ? ld16(bp[n] + k) : zero;
+  // U chunks per trip: all their loads are issued before the first MFMA (a wave's range is a
+  // few dozen chunks at most, so without this each chunk would pay a full memory latency)
+  constexpr int U = 4;
+  auto chunk = [&](const i32x4 a[2], const i32x4 b[2]) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -72,7 +76,47 @@ __global__ __launch_bounds__(256) void router_logits_bf16(const bf16_t* __restri
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[m][n][i] += (double)p[i];
       }
+  };
+  int k = kb;
+  for (; k + 32 * U <= ke; k += 32 * U) {
+    i32x4 a[U][2], b[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) a[u][m] = av[m] ? ld16(ap[m] + k + 32 * u) : zero;
+#pragma unroll
+      for (int n = 0; n < 2; ++n) b[u][n] = bv[n] ? ld16(bp[n] + k + 32 * u) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) chunk(a[u], b[u]);
   }
+  for (; k < ke; k += 32) {
+    i32x4 a[2], b[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) a[m] = av[m] ? ld16(ap[m] + k) : zero;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) b[n] = bv[n] ? ld16(bp[n] + k) : zero;
+    chunk(a, b);
+  }
+
+  if (wave > 0) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave - 1][m * 8 + n * 4 + i][lane] = acc[m][n][i];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[m][n][i] += red[w][m * 8 + n * 4 + i][lane];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -85,21 +129,6 @@ __global__ __launch_bounds__(256) void router_logits_bf16(const bf16_t* __restri
         if (t < T) zpart[((size_t)split * T + t) * E + e] = acc[m][n][i];
       }
     }
-}
-
-// Sum the per-slice fp64 partial logits in slice order and round once to fp32.
-__global__ __launch_bounds__(256) void router_reduce(const double* __restrict__ zpart, int nsplit, int64_t n,
-                                                     float* __restrict__ z) {
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  double part[16];
-#pragma unroll
-  for (int p = 0; p < 16; ++p) part[p] = p < nsplit ? zpart[(size_t)p * n + i] : 0.0;
-  double acc = 0.0;
-#pragma unroll
-  for (int p = 0; p < 16; ++p)
-    if (p < nsplit) acc += part[p];
-  z[i] = (float)acc;
 }
 
 // fp32 inputs: each product is exact in fp64; one thread per (token, expert).
@@ -116,120 +145,187 @@ __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Steps 2-4, one wave per token. Per-wave LDS: s[E], sb[E], group scores, keep flags.
-// Ties everywhere resolve to the lower index; the chosen experts come out in
-// descending selection score.
+// Steps 2-4; TT threads per token (a whole 256-thread block for small batches, one wave
+// otherwise); thread i of a token owns experts i, i + TT, ...
+//   - z: the token's fp64 partial logits summed in slice order, rounded once to fp32
+//   - s = sigmoid(z) (fp64, rounded to fp32), selection score sb = s + bias
+//   - group score: best + second-best sb of the group (best alone without bias); groups of
+//     2..64 experts (a power of two) sit on consecutive lanes and a butterfly finds them,
+//     otherwise one thread per group scans it in LDS
+//   - keep the Gk best groups (ties: lower group); experts of other groups drop to -inf
+//   - choices in descending sb, ties to the lower index: with a block per token every expert
+//     counts the masked scores ranked before it (rank k < K makes it choice k); with a wave per
+//     token, K rounds of wave argmax
+//   - weights: the chosen experts' s over their sum taken in choice order, times route_scale
 // ---------------------------------------------------------------------------
 constexpr int kMaxE = 1024, kMaxG = 64, kMaxK = 16;
 
-__global__ __launch_bounds__(256) void router_select(const double* __restrict__ zpart, const float* __restrict__ z32,
+MOE_DEV void top2_merge(float& b, float& c, float b2, float c2) {
+  const float hi = fmaxf(b, b2), lo = fminf(b, b2);
+  c = fmaxf(lo, fmaxf(c, c2));
+  b = hi;
+}
+
+// TPB tokens per block, TT = 256 / TPB threads per token, EPT experts per thread (E <= TT * EPT).
+template <int EPT, int TPB>
+__global__ __launch_bounds__(256) void router_select(const double* __restrict__ zpart, int nsplit,
                                                      const float* __restrict__ bias, int T, int E, int G, int Gk,
                                                      int K, float route_scale, int32_t* __restrict__ idx_out,
                                                      float* __restrict__ w_out) {
 #pragma clang fp contract(off)
-  extern __shared__ float smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  const bool active = t < T;
-  float* s = smem + wave * (2 * E + 2 * kMaxG);
-  float* sb = s + E;
-  float* gsc = sb + E;
-  int* keep = reinterpret_cast<int*>(gsc + kMaxG);
+  constexpr int TT = 256 / TPB;
+  __shared__ __attribute__((aligned(16))) float s_all[TPB][TT * EPT];  // s
+  __shared__ __attribute__((aligned(16))) float m_all[TPB][TT * EPT];  // sb, then sb masked by kept groups
+  __shared__ float gsc_all[TPB][kMaxG];
+  __shared__ int keep_all[TPB][kMaxG];
+  __shared__ int sel_all[TPB][kMaxK];
+  const int tid = threadIdx.x % TT, slot = threadIdx.x / TT;
+  const int t = min(blockIdx.x * TPB + slot, T - 1);  // a block's spare slots redo the last token
+  const bool writer = blockIdx.x * TPB + slot < T;
+  float* s_l = s_all[slot];
+  float* m_l = m_all[slot];
+  float* gsc = gsc_all[slot];
+  int* keep = keep_all[slot];
+  int* sel = sel_all[slot];
   const int gsize = E / G;
+  const bool lanes_path = gsize >= 2 && gsize <= 64 && (gsize & (gsize - 1)) == 0;
 
-  if (active) {
-    for (int e = lane; e < E; e += 64) {
-      const float zf = z32 ? z32[(size_t)t * E + e] : (float)zpart[(size_t)t * E + e];
-      float sv = (float)(1.0 / (1.0 + exp(-(double)zf)));
-      s[e] = sv;
-      sb[e] = bias ? sv + bias[e] : sv;
+  // all partial logits of this thread's experts requested at once
+  const double* zt = zpart + (size_t)t * E;
+  const size_t slice = (size_t)T * E;
+  double part[EPT][kMaxSplit];
+  float bb[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + TT * j;
+#pragma unroll
+    for (int p = 0; p < kMaxSplit; ++p) part[j][p] = (e < E && p < nsplit) ? zt[p * slice + e] : 0.0;
+    bb[j] = (bias && e < E) ? bias[e] : 0.f;
+  }
+  float sbv[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + TT * j;
+    double z = part[j][0];
+#pragma unroll
+    for (int p = 1; p < kMaxSplit; ++p)
+      if (p < nsplit) z += part[j][p];
+    const float zf = (float)z;
+    const float sv = (float)(1.0 / (1.0 + exp(-(double)zf)));
+    sbv[j] = bias ? sv + bb[j] : sv;
+    if (e < E) {
+      s_l[e] = sv;
+      m_l[e] = sbv[j];
+    } else {
+      sbv[j] = -INFINITY;
+    }
+    if (lanes_path) {
+      float b = sbv[j], c = -INFINITY;
+      for (int off = gsize >> 1; off >= 1; off >>= 1) top2_merge(b, c, __shfl_xor(b, off), __shfl_xor(c, off));
+      if (e < E && e % gsize == 0) gsc[e / gsize] = bias ? b + c : b;
     }
   }
   __syncthreads();
-  if (active && lane < G) {
-    float best = -INFINITY, second = -INFINITY;
-    const float* v = sb + lane * gsize;
-    for (int i = 0; i < gsize; ++i) {
-      float q = v[i];
-      if (q > best) {
-        second = best;
-        best = q;
-      } else if (q > second) {
-        second = q;
-      }
+  if (!lanes_path) {
+    if (tid < G) {
+      float b = -INFINITY, c = -INFINITY;
+      const float* v = m_l + tid * gsize;
+      for (int i = 0; i < gsize; ++i) top2_merge(b, c, v[i], -INFINITY);
+      gsc[tid] = bias ? b + c : b;
     }
-    gsc[lane] = bias ? best + second : best;
+    __syncthreads();
   }
-  __syncthreads();
-  if (active && lane < G) {
-    float mine = gsc[lane];
+  if (tid < G) {
+    const float mine = gsc[tid];
     int rank = 0;
     for (int g = 0; g < G; ++g) {
-      float o = gsc[g];
-      rank += (o > mine) || (o == mine && g < lane);
+      const float o = gsc[g];
+      rank += (o > mine) || (o == mine && g < tid);
     }
-    keep[lane] = (G == 1) || rank < Gk;
+    keep[tid] = (G == 1) || rank < Gk;
   }
   __syncthreads();
-  if (!active) return;
-
-  // masked selection scores owned by this lane: experts lane, lane + 64, ...
-  float m[kMaxE / 64];
-  uint32_t taken = 0;
-  const int nper = (E + 63) / 64;
+  float mv[EPT];
 #pragma unroll
-  for (int j = 0; j < kMaxE / 64; ++j) {
-    int e = lane + 64 * j;
-    m[j] = (j < nper && e < E && keep[e / gsize]) ? sb[e] : -INFINITY;
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + TT * j;
+    mv[j] = (e < E && keep[e / gsize]) ? sbv[j] : -INFINITY;
   }
-  int sel[kMaxK];
+  if constexpr (TT == 64) {
+    // one wave per token: K rounds of wave argmax (ties: lower index)
+    uint32_t taken = 0;
+    for (int k = 0; k < K; ++k) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
 #pragma unroll
-  for (int k = 0; k < kMaxK; ++k) {
-    if (k >= K) continue;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < kMaxE / 64; ++j) {
-      int e = lane + 64 * j;
-      if (j < nper && e < E && !((taken >> j) & 1u) && (m[j] > bv || (m[j] == bv && e < bi))) {
-        bv = m[j];
-        bi = e;
+      for (int j = 0; j < EPT; ++j) {
+        const int e = tid + TT * j;
+        if (e < E && !((taken >> j) & 1u) && (mv[j] > bv || (mv[j] == bv && e < bi))) {
+          bv = mv[j];
+          bi = e;
+        }
       }
-    }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ov = __shfl_xor(bv, off);
-      int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
       }
+      if (tid == 0) sel[k] = bi;
+      if (bi % TT == tid) taken |= 1u << (bi / TT);
     }
-    sel[k] = bi;
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+  } else {
+    // a block per token: each expert counts the masked scores ranked before it
+    __syncthreads();  // every read of the unmasked m_l is done
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int e = tid + TT * j;
+      if (e < E) m_l[e] = mv[j];
+    }
+    __syncthreads();
+    int rank[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) rank[j] = 0;
+    auto count = [&](float o, int e2) {
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) rank[j] += (o > mv[j]) || (o == mv[j] && e2 < tid + TT * j);
+    };
+    const int E4 = E & ~3;
+#pragma unroll 8  // several LDS reads in flight (they are broadcasts: one address per wave)
+    for (int e4 = 0; e4 < E4; e4 += 4) {
+      const float4 q = *reinterpret_cast<const float4*>(m_l + e4);
+      count(q.x, e4);
+      count(q.y, e4 + 1);
+      count(q.z, e4 + 2);
+      count(q.w, e4 + 3);
+    }
+    for (int e2 = E4; e2 < E; ++e2) count(m_l[e2], e2);
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int e = tid + TT * j;
+      if (e < E && rank[j] < K) sel[rank[j]] = e;
+    }
   }
-  // weights: unbiased scores of the chosen experts, divided by their rank-order sum, scaled
-  float tot = s[sel[0]];
-#pragma unroll
-  for (int k = 1; k < kMaxK; ++k)
-    if (k < K) tot = tot + s[sel[k]];
-#pragma unroll
-  for (int k = 0; k < kMaxK; ++k) {
-    if (k < K && lane == k) {
-      float wk = s[sel[k]] / tot;
-      idx_out[(size_t)t * K + k] = sel[k];
-      w_out[(size_t)t * K + k] = wk * route_scale;
-    }
+  __syncthreads();
+  if (writer && tid < K) {
+    float tot = s_l[sel[0]];
+    for (int k = 1; k < K; ++k) tot = tot + s_l[sel[k]];
+    const int e = sel[tid];
+    idx_out[(size_t)t * K + tid] = e;
+    w_out[(size_t)t * K + tid] = s_l[e] / tot * route_scale;
   }
 }
 
 int router_splits(const Dims& d) {
   if (d.dtype == 0) return 1;
-  int64_t row_tiles = (d.T + 31) / 32;
-  int64_t col_tiles = (d.E + 127) / 128;
-  // enough blocks to stream the router weight with many CUs, but few slices to add up
-  int64_t want = (256 + row_tiles * col_tiles - 1) / (row_tiles * col_tiles);
-  int64_t max_split = std::min<int64_t>(16, d.D / 64);
+  int64_t tiles = ((d.T + 31) / 32) * ((d.E + 31) / 32);
+  // enough blocks to stream the router weight with many CUs, but few slices to add up, each
+  // at least one chunk per wave
+  int64_t want = (256 + tiles - 1) / tiles;
+  int64_t max_split = std::min<int64_t>(kMaxSplit, d.D / 128);
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;
   return (int)want;
@@ -249,25 +345,27 @@ hipError_t launch_router_logits(const Dims& d, const void* x, const void* w_gate
                        (const float*)x, (const float*)w_gate, zpart, (int)d.T, d.D, d.E);
   } else {
     int kslice = split_len(d, nsplit);
-    dim3 grid((unsigned)((d.T + 31) / 32), (unsigned)((d.E + 127) / 128), (unsigned)nsplit);
+    dim3 grid((unsigned)((d.T + 31) / 32), (unsigned)((d.E + 31) / 32), (unsigned)nsplit);
     MOE_LAUNCH(router_logits_bf16, grid, dim3(256), 0, s, (const bf16_t*)x, (const bf16_t*)w_gate,
                        zpart, (int)d.T, d.D, d.E, kslice);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_router_select(const Dims& d, const double* zpart, int nsplit, float* z32, const float* bias,
+hipError_t launch_router_select(const Dims& d, const double* zpart, int nsplit, const float* bias,
                                 float route_scale, int32_t* idx, float* w, hipStream_t s) {
   if (d.T == 0) return hipSuccess;
-  const float* zf = nullptr;
-  if (nsplit > 1) {
-    int64_t n = d.T * d.E;
-    MOE_LAUNCH(router_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, zpart, nsplit, n, z32);
-    zf = z32;
-  }
-  size_t lds = 4 * (2 * (size_t)d.E + 2 * kMaxG) * sizeof(float);
-  MOE_LAUNCH(router_select, dim3((unsigned)((d.T + 3) / 4)), dim3(256), lds, s, zpart, zf, bias,
-                     (int)d.T, d.E, d.G, d.Gk, d.K, route_scale, idx, w);
+  // one token per block for small batches (latency), one per wave for large ones with E <= 256
+#define MOE_SELECT(EPT, TPB)                                                                              \
+  MOE_LAUNCH((router_select<EPT, TPB>), dim3((unsigned)((d.T + TPB - 1) / TPB)), dim3(256), 0, s, zpart, nsplit, \
+             bias, (int)d.T, d.E, d.G, d.Gk, d.K, route_scale, idx, w)
+  if (d.T > 256 && d.E <= 64) MOE_SELECT(1, 4);
+  else if (d.T > 256 && d.E <= 128) MOE_SELECT(2, 4);
+  else if (d.T > 256 && d.E <= 256) MOE_SELECT(4, 4);
+  else if (d.E <= 256) MOE_SELECT(1, 1);
+  else if (d.E <= 512) MOE_SELECT(2, 1);
+  else MOE_SELECT(4, 1);
+#undef MOE_SELECT
   return hipGetLastError();
 }
 

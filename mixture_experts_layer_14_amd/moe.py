@@ -24,7 +24,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_CONFIG", -3: "MOE_ERR_WOR
 
 #: Every function include/moe.h declares.
 EXPORTS = ["moe_workspace_size", "moe_route", "moe_dispatch", "moe_forward", "moe_workspace_layout",
-           "moe_status_str", "moe_last_error", "moe_timing_enable", "moe_timing_report"]
+           "moe_status_str", "moe_last_error", "moe_timing_enable", "moe_timing_filter",
+           "moe_timing_report"]
 
 
 class MoeConfig(ctypes.Structure):
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_timing_enable.argtypes = [ctypes.c_int]
         L.moe_timing_enable.restype = ctypes.c_int
+        L.moe_timing_filter.argtypes = [ctypes.c_char_p]
+        L.moe_timing_filter.restype = ctypes.c_int
         L.moe_timing_report.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
         L.moe_timing_report.restype = ctypes.c_int
         L.moe_last_error.argtypes = []
@@ -133,6 +136,11 @@ def forward(cfg: MoeConfig, wts: MoeWeights, x, out, ws, stream=None, tokens: Op
 
 def timing_enable(on: bool):
     _check(lib().moe_timing_enable(1 if on else 0), "moe_timing_enable")
+
+
+def timing_filter(name_part: Optional[str]):
+    """Record spans only for kernels whose name contains name_part (None: all kernels)."""
+    _check(lib().moe_timing_filter(name_part.encode() if name_part else None), "moe_timing_filter")
 
 
 def timing_report() -> dict:

@@ -29,6 +29,11 @@ SMALL = {
                  n_shared=1, route_scale=2.5, dtype="fp8"),
     "wide_bf16": S("wide_bf16", tokens=700, dim=768, n_experts=16, n_groups=4, topk_groups=2, topk=4, inter=256,
                    n_shared=1, route_scale=2.5, dtype="bf16", hot_bias=0.5),
+    # more experts than threads in a block: several experts per router thread
+    "many_experts_bf16": S("many_experts_bf16", tokens=300, dim=256, n_experts=512, n_groups=16, topk_groups=4,
+                           topk=8, inter=64, n_shared=1, route_scale=2.5, dtype="bf16"),
+    "max_experts_bf16": S("max_experts_bf16", tokens=40, dim=256, n_experts=1024, n_groups=64, topk_groups=8,
+                          topk=16, inter=32, n_shared=1, route_scale=1.0, dtype="bf16"),
 }
 FULL = ["decode_bf16", "prefill_bf16", "skewed_bf16", "prefill_fp8"]
 
