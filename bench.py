@@ -63,22 +63,50 @@ def kernel_units(shape, counts):
     return touched, {"gemm1": (g1_bytes, g1_flops), "gemm2": (g2_bytes, g2_flops)}
 
 
-def source_hash():
+CSRC = os.path.join(ROOT, "mixture_experts_layer_14_amd", "csrc")
+
+
+def kernel_base(name):
+    """'void moe::gemm_ring_bf16<0, 256>(...)' or '(gemm_ring_bf16<0, RBM>)' -> 'gemm_ring_bf16'."""
+    n = name.split("(")[1] if name.startswith("(") else name.split("(")[0]
+    n = n.replace("void ", "").replace("moe::", "").strip()
+    return n.split("<")[0].strip()
+
+
+def kernel_key(name):
+    """Base name plus the first template argument (the mode), the same for the span names of
+    bench.py and the names rocprofv3 prints: '(gemm_ring_bf16<0, RBM>)' -> 'gemm_ring_bf16<0>'."""
+    n = name.split("(")[1] if name.startswith("(") else name.split("(")[0]
+    n = n.replace("void ", "").replace("moe::", "").strip()
+    if "<" not in n:
+        return n
+    base, rest = n.split("<", 1)
+    return f"{base.strip()}<{rest.split(',')[0].split('>')[0].strip()}>"
+
+
+def source_hash(kernel):
+    """Hash of the source file that defines `kernel` plus the shared headers: the counters of a
+    kernel stay valid while none of these change."""
+    base = kernel_base(kernel)
+    files = ["common.h", "kernels.h"]
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith(".hip") and f"void {base}(" in open(os.path.join(CSRC, f)).read():
+            files.append(f)
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "mixture_experts_layer_14_amd", "csrc"))):
-        with open(os.path.join(ROOT, "mixture_experts_layer_14_amd", "csrc", f), "rb") as fh:
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
-    current kernel sources; else None."""
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, if it was
+    taken on the current source of that kernel; else None."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(f"{workload}:{kernel}")
-    if not rec or rec.get("source_hash") != source_hash():
+    rec = json.load(open(path)).get(f"{workload}:{kernel_key(kernel)}")
+    if not rec or rec.get("source_hash") != source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
