@@ -85,10 +85,10 @@ def kernel_key(name):
 
 
 def source_hash(kernel):
-    """Hash of the source file that defines `kernel` plus the shared headers: the counters of a
-    kernel stay valid while none of these change."""
+    """Hash of the source file that defines `kernel` plus the headers: the counters of a kernel
+    stay valid while none of these change."""
     base = kernel_base(kernel)
-    files = ["common.h", "kernels.h"]
+    files = [f for f in sorted(os.listdir(CSRC)) if f.endswith(".h")]
     for f in sorted(os.listdir(CSRC)):
         if f.endswith(".hip") and f"void {base}(" in open(os.path.join(CSRC, f)).read():
             files.append(f)

@@ -97,6 +97,7 @@ bool wide_fp8_ok(const Dims& d);
 hipError_t launch_wide_fp8(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
 // 256-row bf16 kernels fed by a direct-to-LDS 3-stage ring (dim % 128, inter % 64)
 bool ring_ok(const Dims& d);
+
 hipError_t launch_ring_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
 // 128-row LDS-tiled bf16 kernels (prefill-sized batches)
 bool wide_ok(const Dims& d);
@@ -117,6 +118,7 @@ MOE_DEV int swz(int row, int chunk) { return row * 128 + ((chunk ^ swz_key(row))
 struct WideItem {
   Tile tl;
   int nt;
+  int mt;  // m-tiles of the item's expert (how often its weight tiles are read)
   bool shared;
 };
 
@@ -141,6 +143,7 @@ MOE_DEV WideItem wide_item(int item, const Tile* __restrict__ tiles, int nr, con
   const int local = local_item - (first - base_tiles) * per;
   WideItem w;
   w.nt = local / mt;
+  w.mt = mt;
   w.tl = tiles[first + local % mt];
   w.shared = probe.expert == E;
   return w;
