@@ -1,0 +1,48 @@
+"""bench.py's host-side contract, without a GPU: the multi-GPU refusal and the helpers that tie
+the rocprofv3 traffic summaries to the current kernel sources."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_before_touching_a_device():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_kernel_names_from_spans_and_from_the_profiler_agree():
+    # the bench's span names (macro text) and rocprofv3's demangled names map to the same key
+    assert bench.kernel_key("(gemm_ring_bf16<0, RBM, RBN, RBK, RST>)") == "gemm_ring_bf16<0>"
+    assert bench.kernel_key("void moe::gemm_ring_bf16<0, 256, 256, 64, 2>(unsigned short const*, int)") == \
+        "gemm_ring_bf16<0>"
+    assert bench.kernel_key("moe::gemm1_stream_bf16(unsigned short const*, int const*)") == "gemm1_stream_bf16"
+    assert bench.kernel_key("gemm1_stream_bf16") == "gemm1_stream_bf16"
+    assert bench.kernel_key("void moe::combine<true>(int const*, float const*)") == "combine<true>"
+    assert bench.kernel_base("(router_select<1, 1>)") == "router_select"
+
+
+def test_source_hash_covers_the_defining_file():
+    h = bench.source_hash("gemm1_stream_bf16")
+    assert h == bench.source_hash("moe::gemm1_stream_bf16(int)")
+    assert h != bench.source_hash("combine<true>")  # different defining file
+
+
+def test_committed_traffic_entries_are_well_formed():
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    recs = json.load(open(path))
+    assert recs
+    for key, rec in recs.items():
+        workload, kernel = key.split(":", 1)
+        assert workload in ("decode_bf16", "prefill_bf16", "skewed_bf16", "prefill_fp8")
+        assert rec["bytes_per_launch"] > 0
+        assert abs(rec["fetch_scale"] - 2.0) < 0.01 and abs(rec["write_scale"] - 1.0) < 0.01
+        assert len(rec["source_hash"]) == 16
