@@ -202,3 +202,31 @@ def test_deterministic_reruns(name):
     assert torch.equal(a, b)
     lay = blk.layout(shape.tokens)
     assert torch.equal(ws_a[lay.idx:lay.o_shared], blk.ws[lay.idx:lay.o_shared])
+
+
+@pytest.mark.parametrize("name", ["decode_bf16", "mid_fp8"])
+def test_graph_replay_matches_eager(name):
+    """The whole forward captured in a HIP graph (nothing in it allocates or memsets) replays to
+    the eager result, every time, with eager launches and synchronisations in between."""
+    shape = inputs.WORKLOADS[name] if name in inputs.WORKLOADS else SMALL[name]
+    say(f"[graph] {name}")
+    tens = inputs.generate(shape, seed=7, device=DEV)
+    blk = moe.Block(tens, shape.tokens)
+    ref = blk.forward(tens.x).clone()
+    out = torch.empty_like(ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        blk.forward(tens.x, out)  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        blk.forward(tens.x, out)
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        blk.forward(tens.x)  # eager work between replays
+        torch.cuda.synchronize()
