@@ -163,6 +163,7 @@ __global__ __launch_bounds__(256, kWideBlocksPerCU) void gemm_wide_bf16(
 bool wide_ok(const Dims& d) { return d.dtype == 1 && d.D % 128 == 0 && d.I % 64 == 0 && d.S % 64 == 0; }
 
 hipError_t launch_wide_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s) {
+  if (wstream_ok(d)) return launch_wstream_bf16(d, w, a, s);
   if (ring_ok(d)) return launch_ring_bf16(d, w, a, s);
   MOE_LAUNCH(gemm_wide_bf16<0>, dim3(kWideGrid), dim3(256), 0, s, (const bf16_t*)a.x, nullptr, nullptr, a.row_token,
              a.offsets, a.tiles_wide, a.meta, (const bf16_t*)w.w1, (const bf16_t*)w.w3, (const bf16_t*)w.ws1,

@@ -99,6 +99,10 @@ hipError_t launch_wide_fp8(const Dims& d, const ExpertPtrs& w, const Act& a, hip
 bool ring_ok(const Dims& d);
 
 hipError_t launch_ring_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
+// 256-row bf16 kernels with a weight stream per wave and a shared activation ring (dim % 256,
+// inter % 128)
+bool wstream_ok(const Dims& d);
+hipError_t launch_wstream_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
 // 128-row LDS-tiled bf16 kernels (prefill-sized batches)
 bool wide_ok(const Dims& d);
 hipError_t launch_wide_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
