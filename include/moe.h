@@ -64,6 +64,13 @@ typedef enum {
  *           128 columns (scale = amax / 448, or 1 when amax = 0). */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8 = 2 } moe_dtype;
 
+/* Router scoring (the Gate.forward excerpt's two branches):
+ * MOE_SCORE_SIGMOID: s = sigmoid(z); weights = chosen s / their sum * route_scale
+ *                    (DeepSeek-V3).
+ * MOE_SCORE_SOFTMAX: s = softmax(z) over the token's experts; weights = chosen s
+ *                    * route_scale, not renormalised. */
+typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score_func;
+
 /* Field names follow the Gate / MoE constructors on the pages. */
 typedef struct {
   int32_t dim;          /* D: 7168 in DeepSeek-V3 */
@@ -75,6 +82,7 @@ typedef struct {
   int32_t n_shared;     /* shared experts, fused into one MLP of hidden n_shared*I: 1 */
   float route_scale;    /* 2.5 */
   int32_t dtype;        /* moe_dtype */
+  int32_t score_func;   /* moe_score_func: MOE_SCORE_SIGMOID in DeepSeek-V3 */
 } moe_config;
 
 /* Block weights, all device pointers, row-major, linear-layer [out, in] layout.
@@ -106,8 +114,9 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes);
  *                 equal scores in ascending expert order
  *   w     [T, K]  fp32 out: routing weights aligned with idx
  * Logits are fp32 values of exact dot products (bf16 or fp32 products summed in
- * fp64 per 32-element chunk), sigmoid is evaluated in fp64, the weight sum runs
- * in rank order. */
+ * fp64 per 32-element chunk); sigmoid, or softmax over the token's experts, is
+ * evaluated in fp64 and rounded once; the sigmoid weights' sum runs in rank
+ * order. n_groups = 1 is plain top-k over all experts. */
 moe_status moe_route(const moe_config* cfg, const void* w_gate, const float* bias, const void* x,
                      int64_t T, int32_t* idx, float* w, void* ws, size_t ws_bytes, void* stream);
 

@@ -36,6 +36,8 @@ moe_status check_config(const moe_config* c, int64_t T, moe::Dims* d) {
   if (T < 0) return fail(MOE_ERR_ARG, "T < 0");
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16 && c->dtype != MOE_FP8)
     return fail(MOE_ERR_CONFIG, "unknown dtype");
+  if (c->score_func != MOE_SCORE_SIGMOID && c->score_func != MOE_SCORE_SOFTMAX)
+    return fail(MOE_ERR_CONFIG, "unknown score_func");
   if (c->dim <= 0 || c->n_experts <= 0 || c->n_groups <= 0 || c->topk_groups <= 0 || c->topk <= 0 ||
       c->inter <= 0 || c->n_shared <= 0)
     return fail(MOE_ERR_CONFIG, "every size in cfg must be positive");
@@ -284,7 +286,7 @@ moe_status moe_route(const moe_config* cfg, const void* w_gate, const float* bia
   double* zpart = at<double>(ws, L.zpart);
   if ((st = hip_status(moe::launch_router_logits(d, x, w_gate, zpart, L.nsplit, s), "router logits")) != MOE_OK)
     return st;
-  return hip_status(moe::launch_router_select(d, zpart, L.nsplit, bias, cfg->route_scale, idx, w, s),
+  return hip_status(moe::launch_router_select(d, zpart, L.nsplit, bias, cfg->route_scale, cfg->score_func == MOE_SCORE_SOFTMAX, idx, w, s),
                     "router select");
 }
 
@@ -339,7 +341,8 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wts, const void
     return st;
   if ((st = hip_status(moe::launch_router_logits(d, x, wts->w_gate, zpart, L.nsplit, s), "router logits")) != MOE_OK)
     return st;
-  if ((st = hip_status(moe::launch_router_select(d, zpart, L.nsplit, wts->bias, cfg->route_scale, idx, w, s),
+  if ((st = hip_status(moe::launch_router_select(d, zpart, L.nsplit, wts->bias, cfg->route_scale, cfg->score_func == MOE_SCORE_SOFTMAX, idx,
+                                                       w, s),
                        "router select")) != MOE_OK)
     return st;
   if ((st = hip_status(moe::launch_dispatch(d, idx, at<int32_t>(ws, L.blk), at<int32_t>(ws, L.pub.counts), offsets,

@@ -51,9 +51,10 @@ struct Dims {
 int router_splits(const Dims& d);
 hipError_t launch_router_logits(const Dims& d, const void* x, const void* w_gate, double* zpart, int nsplit,
                                 hipStream_t s);
-// Sums the nsplit slices of zpart per token in slice order, then scores, groups and selects.
+// Sums the nsplit slices of zpart per token in slice order, then scores (sigmoid, or softmax over
+// the token's experts), groups and selects.
 hipError_t launch_router_select(const Dims& d, const double* zpart, int nsplit, const float* bias,
-                                float route_scale, int32_t* idx, float* w, hipStream_t s);
+                                float route_scale, bool softmax, int32_t* idx, float* w, hipStream_t s);
 
 // ---- dispatch
 int dispatch_blocks(int64_t T);

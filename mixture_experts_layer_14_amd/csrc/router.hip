@@ -222,7 +222,9 @@ __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict
 // Steps 2-4; TT threads per token (a whole 256-thread block for small batches, one wave
 // otherwise); thread i of a token owns experts i, i + TT, ...
 //   - z: the token's fp64 partial logits summed in slice order, rounded once to fp32
-//   - s = sigmoid(z) (fp64, rounded to fp32), selection score sb = s + bias
+//   - s = sigmoid(z), or with softmax scoring s = exp(z - max z) / sum exp(z - max z) over the
+//     token's experts (fp64, the sum taken per thread, then per wave in lane order, then over the
+//     waves in order; rounded once to fp32); selection score sb = s + bias
 //   - group score: best + second-best sb of the group (best alone without bias); groups of
 //     2..64 experts (a power of two) sit on consecutive lanes and a butterfly finds them,
 //     otherwise one thread per group scans it in LDS
@@ -231,8 +233,40 @@ __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict
 //     counts the masked scores ranked before it (rank k < K makes it choice k); with a wave per
 //     token, K rounds of wave argmax
 //   - weights: the chosen experts' s over their sum taken in choice order, times route_scale
+//     (softmax scoring: the chosen s times route_scale, not renormalised)
 // ---------------------------------------------------------------------------
 constexpr int kMaxE = 1024, kMaxG = 64, kMaxK = 16;
+
+// Reductions over the TT threads of one token: a wave (TT = 64) or the whole block (TT = 256,
+// the wave results combined in wave order through sh[4]).
+template <int TT>
+MOE_DEV float token_max(float v, double* sh) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  if constexpr (TT == 64) {
+    return v;
+  } else {
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const float r = fmaxf(fmaxf((float)sh[0], (float)sh[1]), fmaxf((float)sh[2], (float)sh[3]));
+    __syncthreads();
+    return r;
+  }
+}
+template <int TT>
+MOE_DEV double token_sum(double v, double* sh) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  if constexpr (TT == 64) {
+    return v;
+  } else {
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const double r = ((sh[0] + sh[1]) + sh[2]) + sh[3];
+    __syncthreads();
+    return r;
+  }
+}
 
 MOE_DEV void top2_merge(float& b, float& c, float b2, float c2) {
   const float hi = fmaxf(b, b2), lo = fminf(b, b2);
@@ -244,8 +278,8 @@ MOE_DEV void top2_merge(float& b, float& c, float b2, float c2) {
 template <int EPT, int TPB>
 __global__ __launch_bounds__(256) void router_select(const double* __restrict__ zpart, int nsplit,
                                                      const float* __restrict__ bias, int T, int E, int G, int Gk,
-                                                     int K, float route_scale, int32_t* __restrict__ idx_out,
-                                                     float* __restrict__ w_out) {
+                                                     int K, float route_scale, int softmax,
+                                                     int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
 #pragma clang fp contract(off)
   constexpr int TT = 256 / TPB;
   __shared__ __attribute__((aligned(16))) float s_all[TPB][TT * EPT];  // s
@@ -253,6 +287,7 @@ __global__ __launch_bounds__(256) void router_select(const double* __restrict__ 
   __shared__ float gsc_all[TPB][kMaxG];
   __shared__ int keep_all[TPB][kMaxG];
   __shared__ int sel_all[TPB][kMaxK];
+  __shared__ double red[4];  // block-wide reductions (one token per block)
   const int tid = threadIdx.x % TT, slot = threadIdx.x / TT;
   const int t = min(blockIdx.x * TPB + slot, T - 1);  // a block's spare slots redo the last token
   const bool writer = blockIdx.x * TPB + slot < T;
@@ -276,16 +311,35 @@ __global__ __launch_bounds__(256) void router_select(const double* __restrict__ 
     for (int p = 0; p < kMaxSplit; ++p) part[j][p] = (e < E && p < nsplit) ? zt[p * slice + e] : 0.0;
     bb[j] = (bias && e < E) ? bias[e] : 0.f;
   }
-  float sbv[EPT];
+  float zf[EPT];
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
-    const int e = tid + TT * j;
     double z = part[j][0];
 #pragma unroll
     for (int p = 1; p < kMaxSplit; ++p)
       if (p < nsplit) z += part[j][p];
-    const float zf = (float)z;
-    const float sv = (float)(1.0 / (1.0 + exp(-(double)zf)));
+    zf[j] = (float)z;
+  }
+  float zmax = 0.f;
+  double zsum = 1.0;
+  if (softmax) {  // uniform: every thread of the token takes part in the reductions
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j)
+      if (tid + TT * j < E) mx = fmaxf(mx, zf[j]);
+    zmax = token_max<TT>(mx, red);
+    double sm = 0.0;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j)
+      if (tid + TT * j < E) sm += exp((double)zf[j] - (double)zmax);
+    zsum = token_sum<TT>(sm, red);
+  }
+  float sbv[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + TT * j;
+    const float sv = softmax ? (float)(exp((double)zf[j] - (double)zmax) / zsum)
+                             : (float)(1.0 / (1.0 + exp(-(double)zf[j])));
     sbv[j] = bias ? sv + bb[j] : sv;
     if (e < E) {
       s_l[e] = sv;
@@ -385,11 +439,15 @@ __global__ __launch_bounds__(256) void router_select(const double* __restrict__ 
   }
   __syncthreads();
   if (writer && tid < K) {
-    float tot = s_l[sel[0]];
-    for (int k = 1; k < K; ++k) tot = tot + s_l[sel[k]];
     const int e = sel[tid];
     idx_out[(size_t)t * K + tid] = e;
-    w_out[(size_t)t * K + tid] = s_l[e] / tot * route_scale;
+    if (softmax) {
+      w_out[(size_t)t * K + tid] = s_l[e] * route_scale;
+    } else {
+      float tot = s_l[sel[0]];
+      for (int k = 1; k < K; ++k) tot = tot + s_l[sel[k]];
+      w_out[(size_t)t * K + tid] = s_l[e] / tot * route_scale;
+    }
   }
 }
 
@@ -437,12 +495,12 @@ hipError_t launch_router_logits(const Dims& d, const void* x, const void* w_gate
 }
 
 hipError_t launch_router_select(const Dims& d, const double* zpart, int nsplit, const float* bias,
-                                float route_scale, int32_t* idx, float* w, hipStream_t s) {
+                                float route_scale, bool softmax, int32_t* idx, float* w, hipStream_t s) {
   if (d.T == 0) return hipSuccess;
   // one token per block for small batches (latency), one per wave for large ones with E <= 256
 #define MOE_SELECT(EPT, TPB)                                                                              \
   MOE_LAUNCH((router_select<EPT, TPB>), dim3((unsigned)((d.T + TPB - 1) / TPB)), dim3(256), 0, s, zpart, nsplit, \
-             bias, (int)d.T, d.E, d.G, d.Gk, d.K, route_scale, idx, w)
+             bias, (int)d.T, d.E, d.G, d.Gk, d.K, route_scale, softmax ? 1 : 0, idx, w)
   if (d.T > 256 && d.E <= 64) MOE_SELECT(1, 4);
   else if (d.T > 256 && d.E <= 128) MOE_SELECT(2, 4);
   else if (d.T > 256 && d.E <= 256) MOE_SELECT(4, 4);

@@ -51,6 +51,7 @@ class MoeShape:
     dtype: str  # "f32" | "bf16" | "fp8"
     hot_bias: float = 0.0  # added to the bias of experts e with e % 8 == 0
     has_bias: bool = True
+    score_func: str = "sigmoid"  # router scoring: "sigmoid" or "softmax"
 
     @property
     def shared_inter(self) -> int:

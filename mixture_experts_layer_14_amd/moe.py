@@ -19,6 +19,7 @@ _lib = None
 
 MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 _DTYPE = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8}
+_SCORE = {"sigmoid": 0, "softmax": 1}  # moe_score_func
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_CONFIG", -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP",
           -5: "MOE_ERR_UNSUPPORTED"}
 
@@ -31,7 +32,8 @@ EXPORTS = ["moe_workspace_size", "moe_route", "moe_dispatch", "moe_forward", "mo
 class MoeConfig(ctypes.Structure):
     _fields_ = [("dim", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("n_groups", ctypes.c_int32),
                 ("topk_groups", ctypes.c_int32), ("topk", ctypes.c_int32), ("inter", ctypes.c_int32),
-                ("n_shared", ctypes.c_int32), ("route_scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("n_shared", ctypes.c_int32), ("route_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("score_func", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -87,7 +89,7 @@ def _check(status: int, where: str):
 
 def config(shape: MoeShape) -> MoeConfig:
     return MoeConfig(shape.dim, shape.n_experts, shape.n_groups, shape.topk_groups, shape.topk, shape.inter,
-                     shape.n_shared, shape.route_scale, _DTYPE[shape.dtype])
+                     shape.n_shared, shape.route_scale, _DTYPE[shape.dtype], _SCORE[shape.score_func])
 
 
 def _ptr(t: Optional[torch.Tensor]):

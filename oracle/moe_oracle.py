@@ -34,6 +34,10 @@ Readings where the pages are silent (each is listed in the design notes):
       cast to x's dtype.
   R9  FP8 (OCP e4m3fn, bias 7, max 448, no infinities): scale = amax / 448
       (1 when amax = 0), code = round-to-nearest-even(v / scale), saturating.
+  R10 softmax scoring (the excerpt's other branch): exp(z - max z) over the
+      token's experts divided by their sum, in fp64, rounded once to fp32; the
+      gathered softmax scores are not renormalised (the excerpt renormalises
+      only the sigmoid branch) before the route scale.
 
 Functions and their pins (tests/test_oracle_*.py):
   bf16 / e4m3 codecs      torch's bfloat16 / float8_e4m3fn casts; spec values
@@ -41,6 +45,9 @@ Functions and their pins (tests/test_oracle_*.py):
   router_logits           exact rational dot product (fractions) on tiny inputs;
                           identity router weight gives z = x
   sigmoid32               scipy.special.expit; sigma(0) = 0.5
+  softmax scoring         scipy.special.softmax; weights are the gathered
+                          scores times the scale; shift invariance; no-bias
+                          single group = top-k of z; group-max brute force
   route                   brute-force enumeration of group and expert subsets;
                           hand-worked group-score case; invariants (8 distinct,
                           <= 4 groups, sum 2.5); bias-shift invariance;
@@ -187,8 +194,11 @@ class Route:
 
 
 def route_from_logits(cfg, z: np.ndarray, bias: Optional[np.ndarray],
-                      score_func: str = "sigmoid") -> Route:
-    """Steps 2-4 on fp32 logits z [T, E]."""
+                      score_func: Optional[str] = None) -> Route:
+    """Steps 2-4 on fp32 logits z [T, E]. score_func: "sigmoid" or "softmax" (the excerpt's two
+    branches); None takes cfg.score_func, else sigmoid."""
+    if score_func is None:
+        score_func = getattr(cfg, "score_func", "sigmoid")
     z = np.asarray(z, f32)
     t, e = z.shape
     g, gk, k = cfg.n_groups, cfg.topk_groups, cfg.topk
@@ -224,7 +234,7 @@ def route_from_logits(cfg, z: np.ndarray, bias: Optional[np.ndarray],
 
 
 def route(cfg, x: np.ndarray, w_gate: np.ndarray, bias: Optional[np.ndarray],
-          score_func: str = "sigmoid") -> Route:
+          score_func: Optional[str] = None) -> Route:
     """The router: (weights [T, K] fp32, indices [T, K]) for tokens x [T, D]."""
     return route_from_logits(cfg, router_logits(x, w_gate), bias, score_func)
 

@@ -46,7 +46,17 @@ def route_check(shape, oracle_route, gpu_idx, gpu_w):
     ok = ~bad
     ulp = np.abs(gw[ok].view(np.int32).astype(np.int64) - ow[ok].view(np.int32).astype(np.int64))
     rep["w_max_ulp"] = int(ulp.max()) if ulp.size else 0
-    assert rep["w_max_ulp"] <= 4, rep
+    if getattr(shape, "score_func", "sigmoid") == "softmax":
+        # A softmax weight depends on every logit of its token: with logit errors |dz| (the
+        # kernel's 32-product chunks are rounded to fp32 before their fp64 sum, <= ~1e-6 at
+        # these sizes, plus the final rounding) its relative error is at most
+        # |dz_e| + sum_j s_j |dz_j| <= 2 max |dz|; allowed: 4e-6.
+        rel = np.abs(gw[ok].astype(np.float64) - ow[ok]) / np.abs(ow[ok].astype(np.float64))
+        rep["w_max_rel"] = float(rel.max()) if rel.size else 0.0
+        assert rep["w_max_rel"] <= 4e-6, rep
+    else:
+        # a sigmoid weight depends on its own logit and the K chosen scores: <= 4 ulp
+        assert rep["w_max_ulp"] <= 4, rep
     return bad, rep
 
 

@@ -74,6 +74,17 @@ def test_bad_configs_rejected(kw, code):
     assert moe.lib().moe_last_error() != b""
 
 
+def test_score_func_field():
+    """The config's last field selects the router scoring; values other than sigmoid (0) and
+    softmax (1) are configuration errors."""
+    assert moe.MoeConfig._fields_[-1][0] == "score_func"
+    assert status_of_size(cfg_of(score_func="softmax"))[0] == 0
+    c = cfg_of()
+    c.score_func = 2
+    assert status_of_size(c)[0] == -2
+    assert b"score_func" in moe.lib().moe_last_error()
+
+
 def test_negative_tokens_rejected():
     assert status_of_size(cfg_of(), -1)[0] == -1
 

@@ -34,6 +34,18 @@ SMALL = {
                            topk=8, inter=64, n_shared=1, route_scale=2.5, dtype="bf16"),
     "max_experts_bf16": S("max_experts_bf16", tokens=40, dim=256, n_experts=1024, n_groups=64, topk_groups=8,
                           topk=16, inter=32, n_shared=1, route_scale=1.0, dtype="bf16"),
+    # the router's other branches: softmax scoring (a wave per token here), softmax without bias
+    # (groups scored by their best expert; a block per token), one group (plain top-k)
+    "softmax_bf16": S("softmax_bf16", tokens=300, dim=512, n_experts=64, n_groups=8, topk_groups=4, topk=8,
+                      inter=256, n_shared=1, route_scale=2.5, dtype="bf16", score_func="softmax"),
+    "softmax_groupmax_bf16": S("softmax_groupmax_bf16", tokens=200, dim=512, n_experts=64, n_groups=8,
+                               topk_groups=3, topk=6, inter=128, n_shared=1, route_scale=1.0, dtype="bf16",
+                               has_bias=False, score_func="softmax"),
+    "single_group_bf16": S("single_group_bf16", tokens=280, dim=256, n_experts=32, n_groups=1, topk_groups=1,
+                           topk=6, inter=96, n_shared=1, route_scale=2.5, dtype="bf16"),
+    "softmax_single_group_f32": S("softmax_single_group_f32", tokens=50, dim=128, n_experts=16, n_groups=1,
+                                  topk_groups=1, topk=4, inter=64, n_shared=1, route_scale=1.0, dtype="f32",
+                                  has_bias=False, score_func="softmax"),
 }
 FULL = ["decode_bf16", "prefill_bf16", "skewed_bf16", "prefill_fp8"]
 

@@ -213,3 +213,70 @@ def test_dispatch_vs_lexsort(t, e, k):
         for j in range(k):
             row = row_of[tt, j]
             assert row_token[row] == tt and offsets[idx[tt, j]] <= row < offsets[idx[tt, j] + 1]
+
+
+# ---- softmax scoring (the Gate.forward excerpt's softmax branch; reading R10)
+def scfg(**kw):
+    c = cfg(**kw)
+    c.score_func = "softmax"
+    return c
+
+
+def test_softmax_scores_match_scipy():
+    rng = np.random.default_rng(40)
+    z = (rng.standard_normal((200, 64)) * 3).astype(np.float32)
+    r = O.route_from_logits(scfg(E=64, G=1, Gk=1, K=8), z, None)
+    ref = scipy.special.softmax(z.astype(np.float64), axis=1).astype(np.float32)
+    ulps = np.abs(r.s.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1 and (ulps > 0).mean() < 0.01
+
+
+def test_softmax_weights_are_gathered_scores_times_scale():
+    rng = np.random.default_rng(41)
+    z = rng.standard_normal((30, 16)).astype(np.float32)
+    # every expert chosen, scale 1: the weights are the whole distribution and sum to one
+    r = O.route_from_logits(scfg(E=16, G=1, Gk=1, K=16, scale=1.0), z, None)
+    assert np.allclose(r.w.astype(np.float64).sum(1), 1.0, rtol=0, atol=4e-7)
+    # K < E: the gathered scores times the scale, one rounding, no renormalisation
+    r = O.route_from_logits(scfg(E=16, G=1, Gk=1, K=4, scale=2.5), z, None)
+    gathered = np.take_along_axis(r.s, r.idx.astype(np.int64), 1)
+    assert np.array_equal(r.w, (gathered * np.float32(2.5)).astype(np.float32))
+    assert (r.w.astype(np.float64).sum(1) < 2.5).all()
+
+
+def test_softmax_no_bias_single_group_is_topk_of_logits():
+    rng = np.random.default_rng(42)
+    z = rng.standard_normal((60, 32)).astype(np.float32) * 2
+    r = O.route_from_logits(scfg(E=32, G=1, Gk=1, K=6), z, None)
+    for t in range(60):
+        ref = sorted(range(32), key=lambda e: (-float(z[t, e]), e))[:6]
+        assert r.idx[t].tolist() == ref
+
+
+def test_softmax_shift_invariance():
+    """Logits on a 1/256 grid: z + 1 is exact in fp32, z - max z is unchanged, so the scores and
+    the routing are bit-identical."""
+    rng = np.random.default_rng(43)
+    z = (np.round(rng.standard_normal((40, 16)) * 256) / 256).astype(np.float32)
+    b = rng.uniform(-0.01, 0.01, 16).astype(np.float32)
+    c = scfg(E=16, G=4, Gk=2, K=4)
+    r0, r1 = O.route_from_logits(c, z, b), O.route_from_logits(c, z + np.float32(1.0), b)
+    assert np.array_equal(r0.s, r1.s) and np.array_equal(r0.idx, r1.idx) and np.array_equal(r0.w, r1.w)
+
+
+def test_softmax_group_max_brute_force():
+    """No bias (group score = the group's best score): the kept groups maximise the sum of group
+    maxima over all C(4, 2) group pairs, and the chosen experts maximise the sum of scores over all
+    4-subsets of the kept groups' experts."""
+    rng = np.random.default_rng(44)
+    c = scfg(E=16, G=4, Gk=2, K=4)
+    z = rng.standard_normal((64, 16)).astype(np.float32)
+    r = O.route_from_logits(c, z, None)
+    s = r.s.astype(np.float64)
+    for t in range(64):
+        gmax = [s[t, 4 * g:4 * g + 4].max() for g in range(4)]
+        best_pair = max(itertools.combinations(range(4), 2), key=lambda p: sum(gmax[g] for g in p))
+        assert set(r.kept_groups[t].tolist()) == set(best_pair)
+        pool = [e for g in best_pair for e in range(4 * g, 4 * g + 4)]
+        best = max(itertools.combinations(pool, 4), key=lambda q: sum(s[t, e] for e in q))
+        assert set(r.idx[t].tolist()) == set(best)
