@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["api.hip", "router.hip", "dispatch.hip", "experts.hip", "gemm_stream.hip", "gemm_wide.hip", "gemm_ring.hip",
-           "gemm_wstream.hip",
+           "gemm_wstream.hip", "gemm_wstream_fp8.hip",
            "gemm_wide_fp8.hip", "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -305,7 +305,10 @@ hipError_t launch_experts(const Dims& d, const ExpertPtrs& w, const Act& a, hipS
     if (wide_ok(d) && d.R >= 16 * (int64_t)d.E) return launch_wide_bf16(d, w, a, s);
     return launch_stream_bf16(d, w, a, s);
   }
-  if (wide_fp8_ok(d) && d.R >= 16 * (int64_t)d.E) return launch_wide_fp8(d, w, a, s);
+  if (d.R >= 16 * (int64_t)d.E) {
+    if (wstream_fp8_ok(d)) return launch_wstream_fp8(d, w, a, s);
+    if (wide_fp8_ok(d)) return launch_wide_fp8(d, w, a, s);
+  }
   const int g1 = persistent_grid((const void*)gemm1_fp8_m16, 256);
   const int g2 = persistent_grid((const void*)gemm2_fp8_m16, 256);
   MOE_LAUNCH(gemm1_fp8_m16, dim3(g1), dim3(256), 0, s,

@@ -31,7 +31,7 @@
 // the loop are LDS-destination loads, which the compiler neither reorders nor waits for itself.
 #include <type_traits>
 
-#include "ring.h"
+#include "wstream.h"
 
 namespace moe {
 
@@ -48,8 +48,6 @@ constexpr int WS_BQ = WS_WROWS / 8;                                  // weight l
 constexpr int WS_NM = WS_BM / 32;                                    // 32-row groups of an M-tile
 constexpr int WS_B0 = WS_NA * WS_A_STAGE;                            // LDS offset of the slabs
 constexpr size_t WS_LDS = (size_t)WS_B0 + (size_t)WS_WAVES * WS_NB * WS_SLAB;  // 160 KB
-constexpr int WS_OOB = 0x7fffffff;    // buffer offset past every range: the load returns zeros
-constexpr int WS_RANGE = 0x7ffffff0;  // byte range of the activation resources (tensors < 2 GB)
 
 typedef __bf16 bf16x8w_t __attribute__((ext_vector_type(8)));
 
@@ -57,31 +55,6 @@ MOE_DEV f32x16 mfma32w(i32x4 a, i32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8w_t, a), __builtin_bit_cast(bf16x8w_t, b), c,
                                                  0, 0, 0);
 }
-
-// LDS rows of 128 bytes (8 chunks of 16 bytes): chunk c of row r sits at slot c ^ key(r), with
-// key(r) = (r & 7) ^ ((r >> 3) & 3), a function of r mod 32 only. Any 8 consecutive rows, and
-// the even and the odd rows of 16 consecutive rows, use 8 distinct slots, so a fragment read (32
-// consecutive rows, one chunk) is free of bank conflicts; and because the key repeats every 32
-// rows, the fragment address of every 32-row group is one per-lane base plus a constant. A load
-// instruction fills 8 consecutive rows 8 i .. 8 i + 7 (lane: row 8 i + lane / 8, slot lane % 8),
-// so the lane fetches chunk (lane % 8) ^ (lane / 8) ^ (i % 4).
-MOE_DEV int ws_key(int row) { return (row & 7) ^ ((row >> 3) & 3); }
-MOE_DEV int ws_pos(int row, int chunk) { return row * 128 + ((chunk ^ ws_key(row)) << 4); }
-
-MOE_DEV __amdgpu_buffer_rsrc_t ws_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-
-template <bool NT>
-MOE_DEV void ws_dma(__amdgpu_buffer_rsrc_t r, char* lds_dst, int voff, int soff) {
-  constexpr int AUX = NT ? 2 : 0;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, soff, 0, AUX);
-}
-
-struct WsItem {  // one work item of a block (wave-uniform)
-  int row0, nrows, nt, expert, rot;
-  bool sh, live;
-};
 
 // NT: weight loads nontemporal
 template <int MODE, bool NT>

@@ -104,6 +104,9 @@ hipError_t launch_ring_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hi
 // inter % 128)
 bool wstream_ok(const Dims& d);
 hipError_t launch_wstream_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
+// the fp8 counterpart: 128-k scale-block steps, 8 waves of 32 weight rows (dim % 512, inter % 512)
+bool wstream_fp8_ok(const Dims& d);
+hipError_t launch_wstream_fp8(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
 // 128-row LDS-tiled bf16 kernels (prefill-sized batches)
 bool wide_ok(const Dims& d);
 hipError_t launch_wide_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);

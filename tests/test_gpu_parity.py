@@ -27,6 +27,12 @@ SMALL = {
                           inter=96, n_shared=2, route_scale=2.5, dtype="bf16", hot_bias=0.5),
     "mid_fp8": S("mid_fp8", tokens=200, dim=1024, n_experts=32, n_groups=4, topk_groups=2, topk=6, inter=256,
                  n_shared=1, route_scale=2.5, dtype="fp8"),
+    # the fp8 weight-stream GEMMs (dim and inter multiples of 512): skewed routing gives experts of
+    # several M-tiles, ragged tails and empty experts; the second shape runs the k loop's body
+    "wstream_fp8": S("wstream_fp8", tokens=600, dim=1024, n_experts=16, n_groups=4, topk_groups=2, topk=4,
+                     inter=512, n_shared=1, route_scale=2.5, dtype="fp8", hot_bias=0.5),
+    "wstream_fp8_long": S("wstream_fp8_long", tokens=300, dim=2048, n_experts=8, n_groups=2, topk_groups=1,
+                          topk=2, inter=1024, n_shared=1, route_scale=2.5, dtype="fp8"),
     "wide_bf16": S("wide_bf16", tokens=700, dim=768, n_experts=16, n_groups=4, topk_groups=2, topk=4, inter=256,
                    n_shared=1, route_scale=2.5, dtype="bf16", hot_bias=0.5),
     # more experts than threads in a block: several experts per router thread
@@ -112,7 +118,8 @@ def test_forward_full_shape(name):
 
 
 @pytest.mark.parametrize("name,T", [("mid_bf16", 1), ("mid_bf16", 17), ("mid_bf16", 64), ("mid_fp8", 3),
-                                    ("mid_fp8", 40), ("mid_fp8", 129)])
+                                    ("mid_fp8", 40), ("mid_fp8", 129), ("wstream_fp8", 64),
+                                    ("wstream_fp8", 257)])
 def test_token_counts_edges(name, T):
     shape = SMALL[name].with_tokens(T)
     say(f"[edges] {name} T={T}")
