@@ -209,7 +209,7 @@ def test_fp8_activation_codes_bit_exact():
     assert np.array_equal(O.e4m3_decode(xq), O.e4m3_decode(q))
 
 
-@pytest.mark.parametrize("name", ["mid_bf16", "mid_fp8"])
+@pytest.mark.parametrize("name", ["mid_bf16", "mid_fp8", "wstream_fp8"])
 def test_deterministic_reruns(name):
     shape = SMALL[name]
     tens = inputs.generate(shape, seed=6, device=DEV)
@@ -223,7 +223,7 @@ def test_deterministic_reruns(name):
     assert torch.equal(ws_a[lay.idx:lay.o_shared], blk.ws[lay.idx:lay.o_shared])
 
 
-@pytest.mark.parametrize("name", ["decode_bf16", "mid_fp8"])
+@pytest.mark.parametrize("name", ["decode_bf16", "mid_fp8", "wstream_fp8"])
 def test_graph_replay_matches_eager(name):
     """The whole forward captured in a HIP graph (nothing in it allocates or memsets) replays to
     the eager result, every time, with eager launches and synchronisations in between."""
