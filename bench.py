@@ -4,6 +4,8 @@
 A step is one moe_forward (router -> dispatch -> gate/up GEMM + SwiGLU -> down GEMM -> combine)
 over one batch of synthetic tokens already resident in HBM. The default workload is the full
 block at decode shape: 16 tokens, dim 7168, 256 routed + 1 shared expert (inter 2048), bf16.
+The dense_* workloads time instead one moe_ffn, the first layers' dense SwiGLU feed-forward
+(dim 7168, inter 18,432), through the same GEMM kernels.
 
 Prints one JSON line: tokens/s, ms per step, the dominant kernel's roofline (algorithmic bytes or
 flops per launch over its average duration, from HIP events around that kernel's launches inside
@@ -26,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-block tokens/s + % HBM roofline (decode) / % MFMA peak (prefill), 1 GPU"
+METRIC_DENSE = "dense-FFN tokens/s + % HBM roofline (decode) / % MFMA peak (prefill), 1 GPU"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 
@@ -61,6 +64,16 @@ def kernel_units(shape, counts):
     g2_bytes = w2 + (R * I + T * S) * ab + (R + T) * D * ob
     g2_flops = 2 * D * (R * I + T * S)
     return touched, {"gemm1": (g1_bytes, g1_flops), "gemm2": (g2_bytes, g2_flops)}
+
+
+def ffn_units(shape):
+    """Algorithmic bytes and flops per launch of the dense feed-forward's two GEMM kernels."""
+    D, I, T = shape.dim, shape.inter, shape.tokens
+    wb = 1 if shape.dtype == "fp8" else (4 if shape.dtype == "f32" else 2)
+    ab, ob = wb, (4 if shape.dtype == "f32" else 2)
+    g1 = (2 * I * D * wb + T * D * ab + T * I * ab, 4 * T * D * I)
+    g2 = (I * D * wb + T * I * ab + T * D * ob, 2 * T * D * I)
+    return {"gemm1": g1, "gemm2": g2}
 
 
 CSRC = os.path.join(ROOT, "mixture_experts_layer_14_amd", "csrc")
@@ -111,24 +124,29 @@ def traffic_from_profiles(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(shape, tens, max_tokens, min_seconds=10.0, max_reps=8):
+def cpu_baseline(shape, tens, max_tokens, min_seconds=10.0, max_reps=8, dense=False):
     """The oracle as it stands, on the first `max_tokens` tokens of the same inputs, repeated until
     about `min_seconds` of CPU work (at most `max_reps` passes)."""
     from threadpoolctl import threadpool_info
 
-    from tests.oracle_io import oracle_forward, exact
+    from tests.oracle_io import exact, ffn_mats, oracle_ffn, oracle_forward
 
     n = min(max_tokens, shape.tokens)
     x = exact(tens.x[:n])
+    mats = ffn_mats(tens) if dense else None
     reps, dt = 0, 0.0
     while reps < max_reps and (reps == 0 or dt < min_seconds):
         t0 = time.perf_counter()
-        oracle_forward(tens, x=x)
+        if dense:
+            oracle_ffn(tens, x=x, mats=mats)
+        else:
+            oracle_forward(tens, x=x)
         dt += time.perf_counter() - t0
         reps += 1
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": n * reps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {shape.tokens} tokens of {shape.name}, all their experts, {reps} pass(es), "
+            "sample": f"first {n} of {shape.tokens} tokens of {shape.name}"
+                      f"{'' if dense else ', all their experts'}, {reps} pass(es), "
                       f"seconds={dt:.1f}"}
 
 
@@ -143,7 +161,8 @@ def main():
 
     from mixture_experts_layer_14_amd import inputs, moe
 
-    shape = inputs.WORKLOADS[args.workload]
+    dense = args.workload in inputs.FFN_WORKLOADS
+    shape = inputs.FFN_WORKLOADS[args.workload] if dense else inputs.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     if args.calib_copy_mb:
@@ -155,17 +174,24 @@ def main():
         print(f"[bench] calibration copy of {args.calib_copy_mb} MiB x 3 done", file=sys.stderr, flush=True)
         del src, dst
     print(f"[bench] generating {shape.name} inputs (seed {args.seed})", file=sys.stderr, flush=True)
-    tens = inputs.generate(shape, seed=args.seed, device=dev)
-    blk = moe.Block(tens, shape.tokens)
+    if dense:
+        tens = inputs.generate_ffn(shape, seed=args.seed, device=dev)
+        blk = moe.Ffn(tens, shape.tokens)
+    else:
+        tens = inputs.generate(shape, seed=args.seed, device=dev)
+        blk = moe.Block(tens, shape.tokens)
     out = torch.empty_like(tens.x)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         blk.forward(tens.x, out)
     torch.cuda.synchronize()
 
-    T, K = shape.tokens, shape.topk
-    counts = blk.ws_view(T, "counts", torch.int32, shape.n_experts).cpu().numpy()
-    touched, units = kernel_units(shape, counts)
+    T = shape.tokens
+    if dense:
+        touched, units = None, ffn_units(shape)
+    else:
+        counts = blk.ws_view(T, "counts", torch.int32, shape.n_experts).cpu().numpy()
+        touched, units = kernel_units(shape, counts)
 
     # Per-kernel breakdown: K untimed steps with HIP events around every launch (they add a few
     # microseconds per launch, so the timed steps below keep them on the dominant kernel only).
@@ -215,16 +241,21 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(shape, tens, 16)
+        cpu = cpu_baseline(shape, tens, 16, max_reps=400 if dense else 8, dense=dense)
 
+    if dense:
+        config = {"workload": shape.name, "tokens": T, "dim": shape.dim, "inter": shape.inter, "seed": args.seed}
+    else:
+        config = {"workload": shape.name, "tokens": T, "dim": shape.dim, "experts": shape.n_experts,
+                  "groups": shape.n_groups, "topk_groups": shape.topk_groups, "topk": shape.topk,
+                  "inter": shape.inter, "shared": shape.n_shared, "touched_experts": touched, "seed": args.seed}
     rec = {
-        "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC_DENSE if dense else METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8": "fp8", "f32": "f32"}[shape.dtype], "data": "synthetic",
-        "config": {"workload": shape.name, "tokens": T, "dim": shape.dim, "experts": shape.n_experts,
-                   "groups": shape.n_groups, "topk_groups": shape.topk_groups, "topk": K, "inter": shape.inter,
-                   "shared": shape.n_shared, "touched_experts": touched, "seed": args.seed},
+        "config": config,
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels_ms": {n: round(v[1], 5) for n, v in kernels.items()},

@@ -153,6 +153,47 @@ typedef struct {
 } moe_ws_layout;
 moe_status moe_workspace_layout(const moe_config* cfg, int64_t T, moe_ws_layout* layout);
 
+/* Dense SwiGLU feed-forward of the model's first three layers. "Hardware for
+ * DeepSeek-V3 and R1: Why a 671B MoE Model Needs So Much Memory", section "Why
+ * the dense layers and shared expert matter": those layers are ordinary dense
+ * feed-forward blocks with an intermediate size of 18,432; their MLP has the
+ * form the MoE block page gives its shared expert:
+ *   out[T, D] = W2 (silu(W1 x) * (W3 x)) per token, no biases; the activation h
+ *   is formed in fp32 and stored in the activation dtype (fp32, bf16, or e4m3
+ *   with one fp32 scale per token per 128 columns, x quantised the same way);
+ *   out is stored in x's dtype (fp32 for MOE_F32, bf16 otherwise).
+ * The same GEMM kernels as the block's shared expert, with no router, dispatch
+ * or combine. Conventions as above (device pointers, 16-byte aligned, ws of at
+ * least moe_ffn_workspace_size() bytes, stream-ordered, host-side checks). */
+typedef struct {
+  int32_t dim;    /* D: 7168 in DeepSeek-V3 */
+  int32_t inter;  /* I, the dense intermediate size: 18432 */
+  int32_t dtype;  /* moe_dtype; bf16 needs dim % 128 == 0 and inter % 32 == 0,
+                     fp8 dim and inter multiples of 128 */
+} moe_ffn_config;
+
+/* Dense FFN weights, device pointers, [out, in] row-major:
+ *   w1, w3 [I, D];  w2 [D, I]   (fp32 / bf16 / e4m3fn per dtype)
+ *   FP8 only, fp32 scales per 128x128 block: s1, s3 [I/128, D/128];
+ *   s2 [D/128, I/128]. NULL for other dtypes. */
+typedef struct {
+  const void *w1, *w3, *w2;
+  const float *s1, *s3, *s2;
+} moe_ffn_weights;
+
+/* Bytes of scratch moe_ffn needs for T tokens.
+ * Errors: MOE_ERR_ARG (null, T < 0), MOE_ERR_CONFIG (sizes not positive, unknown
+ * dtype), MOE_ERR_UNSUPPORTED (alignment of dim / inter for the dtype, too many
+ * tokens). */
+moe_status moe_ffn_workspace_size(const moe_ffn_config* cfg, int64_t T, size_t* bytes);
+
+/* out[T, D] = the dense FFN of x[T, D] (fp32 for MOE_F32, bf16 otherwise).
+ * x and out may not overlap. Errors as moe_ffn_workspace_size, plus
+ * MOE_ERR_ARG for NULL or misaligned tensors (fp8 without its scales),
+ * MOE_ERR_WORKSPACE for a short ws, MOE_ERR_HIP for a failed launch. */
+moe_status moe_ffn(const moe_ffn_config* cfg, const moe_ffn_weights* wts, const void* x, int64_t T,
+                   void* out, void* ws, size_t ws_bytes, void* stream);
+
 /* Per-kernel GPU timing, for measurement only (the bench uses it; nothing else needs it).
  * While enabled (on != 0), every kernel the calls above launch is bracketed by a pair of HIP
  * events recorded on its stream; enabling or disabling drops any collected records. Enabling

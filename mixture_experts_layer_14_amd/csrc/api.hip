@@ -105,6 +105,61 @@ Layout plan(const moe::Dims& d) {
   return L;
 }
 
+// A dense feed-forward as a block with no routed experts: E = 0, K = 0, the shared expert of
+// width S = inter on every token (I = S as well, so kernels that take S == I accept it).
+moe_status check_ffn_config(const moe_ffn_config* c, int64_t T, moe::Dims* d) {
+  if (!c) return fail(MOE_ERR_ARG, "cfg is NULL");
+  if (T < 0) return fail(MOE_ERR_ARG, "T < 0");
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16 && c->dtype != MOE_FP8)
+    return fail(MOE_ERR_CONFIG, "unknown dtype");
+  if (c->dim <= 0 || c->inter <= 0) return fail(MOE_ERR_CONFIG, "dim and inter must be positive");
+  if (c->dtype == MOE_BF16 && (c->dim % 128 || c->inter % 32))
+    return fail(MOE_ERR_UNSUPPORTED, "bf16 needs dim % 128 == 0 and inter % 32 == 0");
+  if (c->dtype == MOE_FP8 && (c->dim % 128 || c->inter % 128))
+    return fail(MOE_ERR_UNSUPPORTED, "fp8 needs dim and inter multiples of 128");
+  if (T >= (int64_t)1 << 31 || T * (int64_t)c->dim >= (int64_t)1 << 40 || T * (int64_t)c->inter >= (int64_t)1 << 40)
+    return fail(MOE_ERR_UNSUPPORTED, "too many tokens");
+  d->T = T;
+  d->R = 0;
+  d->D = c->dim;
+  d->E = 0;
+  d->G = 1;
+  d->Gk = 1;
+  d->K = 0;
+  d->I = c->inter;
+  d->S = c->inter;
+  d->dtype = c->dtype;
+  return MOE_OK;
+}
+
+// Workspace of the dense feed-forward: tile lists, x's fp8 image, h (+ scales). The down GEMM
+// writes the output itself.
+Layout plan_ffn(const moe::Dims& d) {
+  Layout L;
+  memset(&L, 0, sizeof(L));
+  const size_t act = d.dtype == MOE_F32 ? 4 : d.dtype == MOE_BF16 ? 2 : 1;
+  const bool fp8 = d.dtype == MOE_FP8;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.pub.offsets = take(4);
+  L.meta = take(moe::kMetaInts * 4);
+  L.tiles_s = take((size_t)moe::max_tiles(d, moe::kSkinnyBM) * sizeof(Tile));
+  L.tiles_w = take((size_t)moe::max_tiles(d, moe::kWideBM) * sizeof(Tile));
+  L.tiles_w2 = take((size_t)moe::max_tiles(d, moe::kWideBM2) * sizeof(Tile));
+  L.pub.xq = take(fp8 ? (size_t)d.T * d.D : 0);
+  L.pub.x_scale = take(fp8 ? (size_t)d.T * (d.D / 128) * 4 : 0);
+  L.pub.h_shared = take((size_t)d.T * d.S * act);
+  L.pub.h_shared_scale = take(fp8 ? (size_t)d.T * (d.S / 128) * 4 : 0);
+  const int split = moe::dense_down_split(d);
+  L.zpart = take(split > 1 ? (size_t)split * d.T * d.D * 4 : 0);  // the down projection's partial sums
+  L.pub.total = o;
+  return L;
+}
+
 template <typename T>
 T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
@@ -369,6 +424,64 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wts, const void
   act.o_shared = at<void>(ws, L.pub.o_shared);
   if ((st = hip_status(moe::launch_experts(d, ep, act, s), "experts")) != MOE_OK) return st;
   return hip_status(moe::launch_combine(d, idx, w, row_of, act.o_routed, act.o_shared, out, s), "combine");
+}
+
+moe_status moe_ffn_workspace_size(const moe_ffn_config* cfg, int64_t T, size_t* bytes) {
+  moe::Dims d;
+  if (!bytes) return fail(MOE_ERR_ARG, "bytes is NULL");
+  moe_status st = check_ffn_config(cfg, T, &d);
+  if (st != MOE_OK) return st;
+  *bytes = plan_ffn(d).pub.total;
+  return MOE_OK;
+}
+
+moe_status moe_ffn(const moe_ffn_config* cfg, const moe_ffn_weights* wts, const void* x, int64_t T, void* out,
+                   void* ws, size_t ws_bytes, void* stream) {
+  moe::Dims d;
+  moe_status st = check_ffn_config(cfg, T, &d);
+  if (st != MOE_OK) return st;
+  if (!wts) return fail(MOE_ERR_ARG, "wts is NULL");
+  if (T == 0) return MOE_OK;
+  if (!x || !out || !wts->w1 || !wts->w3 || !wts->w2) return fail(MOE_ERR_ARG, "NULL tensor argument");
+  const bool fp8 = d.dtype == MOE_FP8;
+  if (fp8 && (!wts->s1 || !wts->s3 || !wts->s2)) return fail(MOE_ERR_ARG, "fp8 weights need their block scales");
+  const void* ptrs[] = {x, out, wts->w1, wts->w3, wts->w2, wts->s1, wts->s3, wts->s2};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(MOE_ERR_ARG, "device pointers must be 16-byte aligned");
+  Layout L = plan_ffn(d);
+  if ((st = check_ws(L, ws, ws_bytes)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  int32_t* offsets = at<int32_t>(ws, L.pub.offsets);
+  int32_t* meta = at<int32_t>(ws, L.meta);
+  if (fp8 && (st = hip_status(moe::launch_act_quant(d, static_cast<const bf16_t*>(x), at<uint8_t>(ws, L.pub.xq),
+                                                    at<float>(ws, L.pub.x_scale), s),
+                              "activation quantisation")) != MOE_OK)
+    return st;
+  if ((st = hip_status(moe::launch_dense_tiles(d, offsets, meta, at<Tile>(ws, L.tiles_s), at<Tile>(ws, L.tiles_w),
+                                               at<Tile>(ws, L.tiles_w2), s),
+                       "tile lists")) != MOE_OK)
+    return st;
+  // the weights take the shared expert's place; there are no routed rows
+  moe::ExpertPtrs ep{nullptr, nullptr, nullptr, wts->w1, wts->w3, wts->w2,
+                     nullptr, nullptr, nullptr, wts->s1, wts->s3, wts->s2};
+  moe::Act act;
+  act.x = fp8 ? static_cast<const void*>(at<uint8_t>(ws, L.pub.xq)) : x;
+  act.x_scale = fp8 ? at<float>(ws, L.pub.x_scale) : nullptr;
+  act.row_token = nullptr;
+  act.offsets = offsets;
+  act.meta = meta;
+  act.tiles_skinny = at<Tile>(ws, L.tiles_s);
+  act.tiles_wide = at<Tile>(ws, L.tiles_w);
+  act.tiles_wide2 = at<Tile>(ws, L.tiles_w2);
+  act.h_routed = nullptr;
+  act.h_shared = at<void>(ws, L.pub.h_shared);
+  act.h_scale = nullptr;
+  act.h_shared_scale = fp8 ? at<float>(ws, L.pub.h_shared_scale) : nullptr;
+  act.o_routed = nullptr;
+  act.o_shared = out;  // the down GEMM's shared-expert output is the result, in x's dtype
+  act.part = moe::dense_down_split(d) > 1 ? at<float>(ws, L.zpart) : nullptr;
+  return hip_status(moe::launch_experts(d, ep, act, s), "dense feed-forward");
 }
 
 const char* moe_status_str(int status) {

@@ -222,6 +222,24 @@ __global__ __launch_bounds__(TB) void dispatch_scatter(const int32_t* __restrict
   scatter_rows(bits, idx, T, K, E, blk + (size_t)blockIdx.x * E, row_token, row_of);
 }
 
+// Tile lists of a dense feed-forward: no routed experts (E = 0), so the lists hold only the
+// shared-expert tiles (expert index E) over all T tokens, written by the same code as the
+// block's dispatch; offsets[0] = 0 and meta as above.
+__global__ __launch_bounds__(TB) void dense_tiles(int T, int32_t* __restrict__ offsets, int32_t* __restrict__ meta,
+                                                  Tile* __restrict__ tiles_s, Tile* __restrict__ tiles_w,
+                                                  Tile* __restrict__ tiles_w2) {
+  __shared__ int cnt[1];
+  __shared__ int off[1];
+  __shared__ int scratch[4];
+  publish(cnt, off, 0, T, nullptr, offsets, meta, tiles_s, tiles_w, tiles_w2, scratch);
+}
+
+hipError_t launch_dense_tiles(const Dims& d, int32_t* offsets, int32_t* meta, Tile* tiles_s, Tile* tiles_w,
+                              Tile* tiles_w2, hipStream_t s) {
+  MOE_LAUNCH(dense_tiles, dim3(1), dim3(TB), 0, s, (int)d.T, offsets, meta, tiles_s, tiles_w, tiles_w2);
+  return hipGetLastError();
+}
+
 int dispatch_blocks(int64_t T) { return (int)((T + TB - 1) / TB); }
 
 int64_t max_tiles(const Dims& d, int bm) { return d.R / bm + d.E + (d.T + bm - 1) / bm + 1; }

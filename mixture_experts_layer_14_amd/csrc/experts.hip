@@ -300,12 +300,14 @@ hipError_t launch_experts(const Dims& d, const ExpertPtrs& w, const Act& a, hipS
                        (float*)a.o_routed, (float*)a.o_shared, d.R, d.T, d.D, d.I, d.S, E);
     return hipGetLastError();
   }
+  // 128-row tiles once the routed experts average 16 rows or more; for a dense feed-forward (no
+  // routed experts) once it has kDenseWideRows tokens
+  const bool wide = d.E > 0 ? d.R >= 16 * (int64_t)d.E : d.T >= kDenseWideRows;
   if (d.dtype == 1) {
-    // 128-row tiles once the routed experts average 16 rows or more
-    if (wide_ok(d) && d.R >= 16 * (int64_t)d.E) return launch_wide_bf16(d, w, a, s);
+    if (wide_ok(d) && wide) return launch_wide_bf16(d, w, a, s);
     return launch_stream_bf16(d, w, a, s);
   }
-  if (d.R >= 16 * (int64_t)d.E) {
+  if (wide) {
     if (wstream_fp8_ok(d)) return launch_wstream_fp8(d, w, a, s);
     if (wide_fp8_ok(d)) return launch_wide_fp8(d, w, a, s);
   }

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(64 * G1_WAVES, 2) void gemm1_stream_bf16(
 struct G2Info {  // wave-uniform
   Tile tl;
   bool sh;
-  int nt, K, rot;
+  int nt, ks, K, ld, rot;  // K: the item's k length (one split's share), ld: the row stride
   SlabStream st;
 };
 
@@ -295,38 +295,48 @@ MOE_DEV int g2_k(const G2Info& g, int k0) {
   return k >= g.K ? k - g.K : k;
 }
 
-MOE_DEV G2Info g2_info(int item, const Tile* tiles, int per, const bf16_t* w2, const bf16_t* ws2, int D, int I,
-                       int S, int E) {
+// item -> (tile, 16-column group nt, k split ks): with ksplit > 1 each item covers the ks-th share
+// of k, reading weights and h from that share's first column on (same row strides).
+MOE_DEV G2Info g2_info(int item, const Tile* tiles, int per, int ksplit, const bf16_t* w2, const bf16_t* ws2, int D,
+                       int I, int S, int E) {
   G2Info g;
-  const int ti = item / per;
-  g.nt = item % per;
+  const int base = item / ksplit;
+  g.ks = item - base * ksplit;
+  const int ti = base / per;
+  g.nt = base % per;
   g.tl = tiles[ti];
   g.sh = g.tl.expert == E;
-  g.K = g.sh ? S : I;
-  g.st = slab_stream((g.sh ? ws2 : w2 + (size_t)g.tl.expert * D * I) + (size_t)g.nt * 16 * g.K, g.K);
+  g.ld = g.sh ? S : I;
+  g.K = g.ld / ksplit;
+  g.st = slab_stream((g.sh ? ws2 : w2 + (size_t)g.tl.expert * D * I) + (size_t)g.nt * 16 * g.ld + (size_t)g.ks * g.K,
+                     g.ld);
   g.rot = g.K % SK == 0 ? ((g.nt * 5 + g.tl.expert * 3) % (g.K / SK)) * SK : 0;
   return g;
 }
 
-// h row of this lane's tile row (rows past the tile's end read the tile's row 0)
+// h row of this lane's tile row (rows past the tile's end read the tile's row 0), from the
+// item's k share on
 MOE_DEV const bf16_t* g2_arow(const G2Info& g, const bf16_t* h_routed, const bf16_t* h_shared, int r) {
   const bf16_t* A = g.sh ? h_shared : h_routed;
-  return A + (size_t)(g.tl.row0 + (r < g.tl.nrows ? r : 0)) * g.K;
+  return A + (size_t)(g.tl.row0 + (r < g.tl.nrows ? r : 0)) * g.ld + (size_t)g.ks * g.K;
 }
 
+// ksplit == 1: o = h W2^T in bf16. ksplit > 1 (shared-expert tiles only): split ks writes its fp32
+// partial sum to part[ks][token][column]; dense_down_sum adds the splits in order.
 __global__ __launch_bounds__(64 * G2_WAVES) void gemm2_stream_bf16(
     const bf16_t* __restrict__ h_routed, const bf16_t* __restrict__ h_shared, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ meta, const bf16_t* __restrict__ w2, const bf16_t* __restrict__ ws2,
-    bf16_t* __restrict__ o_routed, bf16_t* __restrict__ o_shared, int D, int I, int S, int E) {
+    bf16_t* __restrict__ o_routed, bf16_t* __restrict__ o_shared, float* __restrict__ part, int ksplit, int T, int D,
+    int I, int S, int E) {
   __shared__ __attribute__((aligned(16))) char lds[G2_WAVES][SLAB];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, q = lane >> 4;
   const int per = D / 16;
-  const int items = meta[1] * per;
+  const int items = meta[1] * per * ksplit;
   const int stride = gridDim.x * G2_WAVES;
   int item = blockIdx.x * G2_WAVES + wave;
   if (item >= items) return;
-  auto info_at = [&](int it) { return g2_info(it, tiles, per, w2, ws2, D, I, S, E); };
+  auto info_at = [&](int it) { return g2_info(it, tiles, per, ksplit, w2, ws2, D, I, S, E); };
 
   int l_item = item, l_k0 = 0;
   G2Info l = info_at(l_item);
@@ -375,11 +385,19 @@ __global__ __launch_bounds__(64 * G2_WAVES) void gemm2_stream_bf16(
     slab_mma<1>(acc, a, lds[wave], g2_k(c, c_k0), c.K, lane);
     c_k0 += SK;
     if (c_k0 >= c.K) {
-      bf16_t* O = c.sh ? o_shared : o_routed;
+      if (ksplit == 1) {
+        bf16_t* O = c.sh ? o_shared : o_routed;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = q * 4 + i;
-        if (row < c.tl.nrows) O[(size_t)(c.tl.row0 + row) * D + c.nt * 16 + r] = f32_to_bf16(acc[0][i]);
+        for (int i = 0; i < 4; ++i) {
+          const int row = q * 4 + i;
+          if (row < c.tl.nrows) O[(size_t)(c.tl.row0 + row) * D + c.nt * 16 + r] = f32_to_bf16(acc[0][i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = q * 4 + i;
+          if (row < c.tl.nrows) part[((size_t)c.ks * T + c.tl.row0 + row) * D + c.nt * 16 + r] = acc[0][i];
+        }
       }
       acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
       item += stride;
@@ -395,15 +413,43 @@ __global__ __launch_bounds__(64 * G2_WAVES) void gemm2_stream_bf16(
   }
 }
 
+// out[t][c] = bf16( sum over ks ascending of part[ks][t][c] ), fp32 adds
+__global__ __launch_bounds__(256) void dense_down_sum(const float* __restrict__ part, int ksplit, int64_t n,
+                                                      bf16_t* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float v = part[i];
+    for (int ks = 1; ks < ksplit; ++ks) v += part[(size_t)ks * n + i];
+    out[i] = f32_to_bf16(v);
+  }
+}
+
+int dense_down_split(const Dims& d) {
+  // the dense feed-forward's down projection on the 16-row path has ceil(T/16) * D/16 items of
+  // the full inter length; split k until there are about four waves per SIMD (keeping the split a
+  // divisor of inter / 128)
+  if (d.E != 0 || d.dtype != 1 || d.T <= 0 || d.T >= kDenseWideRows || d.S % SK || d.D < 16) return 1;
+  const int64_t items = (d.T + 15) / 16 * (d.D / 16);
+  int want = (int)std::min<int64_t>(16, (4096 + items - 1) / items);
+  while (want > 1 && (d.S / SK) % want) --want;
+  return want;
+}
+
 hipError_t launch_stream_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s) {
   const int g1 = persistent_grid((const void*)gemm1_stream_bf16, 64 * G1_WAVES);
   const int g2 = persistent_grid((const void*)gemm2_stream_bf16, 64 * G2_WAVES);
   MOE_LAUNCH(gemm1_stream_bf16, dim3(g1), dim3(64 * G1_WAVES), 0, s, (const bf16_t*)a.x, a.row_token, a.tiles_skinny,
              a.meta, (const bf16_t*)w.w1, (const bf16_t*)w.w3, (const bf16_t*)w.ws1, (const bf16_t*)w.ws3,
              (bf16_t*)a.h_routed, (bf16_t*)a.h_shared, d.D, d.I, d.S, d.E);
+  const int split = dense_down_split(d);
+  if (split > 1 && !a.part) return hipErrorInvalidValue;  // the caller sized no partial buffer
   MOE_LAUNCH(gemm2_stream_bf16, dim3(g2), dim3(64 * G2_WAVES), 0, s, (const bf16_t*)a.h_routed,
              (const bf16_t*)a.h_shared, a.tiles_skinny, a.meta, (const bf16_t*)w.w2, (const bf16_t*)w.ws2,
-             (bf16_t*)a.o_routed, (bf16_t*)a.o_shared, d.D, d.I, d.S, d.E);
+             (bf16_t*)a.o_routed, (bf16_t*)a.o_shared, a.part, split, (int)d.T, d.D, d.I, d.S, d.E);
+  if (split > 1) {
+    const int64_t n = d.T * d.D;
+    MOE_LAUNCH(dense_down_sum, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 2048)), dim3(256), 0, s, a.part,
+               split, n, (bf16_t*)a.o_shared);
+  }
   return hipGetLastError();
 }
 

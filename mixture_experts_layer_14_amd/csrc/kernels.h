@@ -58,6 +58,9 @@ hipError_t launch_router_select(const Dims& d, const double* zpart, int nsplit, 
 
 // ---- dispatch
 int dispatch_blocks(int64_t T);
+// The tile lists and meta of a dense feed-forward (E = 0: only shared-expert tiles over T tokens).
+hipError_t launch_dense_tiles(const Dims& d, int32_t* offsets, int32_t* meta, Tile* tiles_s, Tile* tiles_w,
+                              Tile* tiles_w2, hipStream_t s);
 hipError_t launch_dispatch(const Dims& d, const int32_t* idx, int32_t* blk, int32_t* counts, int32_t* offsets,
                            int32_t* row_token, int32_t* row_of, int32_t* meta, Tile* tiles_skinny,
                            Tile* tiles_wide, Tile* tiles_wide2, hipStream_t s);
@@ -86,10 +89,15 @@ struct Act {
   float* h_shared_scale;    // fp8: [T, S/128]
   void* o_routed;           // [R, D]
   void* o_shared;           // [T, D]
+  float* part = nullptr;    // [split, T, D] fp32 partial sums of a k-split down projection
 };
 hipError_t launch_experts(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
 // 16-row weight-streaming bf16 kernels (decode-sized batches)
 hipError_t launch_stream_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
+// Dense feed-forward (E = 0): tokens from which the 128-row kernels take over, and the k split of
+// the 16-row down projection below that (1 = none; > 1 needs Act::part of split * T * D floats).
+constexpr int64_t kDenseWideRows = 64;
+int dense_down_split(const Dims& d);
 // Blocks of `kernel` that fit on the current device at once (occupancy x CUs, the occupancy capped
 // at max_per_cu when that is positive), cached per device and kernel.
 int persistent_grid(const void* kernel, int threads, size_t dyn_lds = 0, int max_per_cu = 0);

@@ -200,3 +200,62 @@ def regenerate_x(shape: MoeShape, seed: int = 0, device="cpu") -> torch.Tensor:
     act = torch.float32 if shape.dtype == "f32" else torch.bfloat16
     return torch.randn(shape.tokens, shape.dim, generator=_gen(torch.device(device), seed, _TID["x"]),
                        device=device, dtype=torch.float32).to(act)
+
+
+# --------------------------------------------------------------------------
+# Dense feed-forward of the first layers ("Hardware for DeepSeek-V3 and R1",
+# section "Why the dense layers and shared expert matter": intermediate 18,432)
+# --------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class FfnShape:
+    """One dense SwiGLU feed-forward workload: tokens x dim -> inter -> dim."""
+
+    name: str
+    tokens: int
+    dim: int
+    inter: int
+    dtype: str  # "f32" | "bf16" | "fp8"
+
+    def with_tokens(self, t: int) -> "FfnShape":
+        return dataclasses.replace(self, tokens=t)
+
+
+#: The dense layer at the block's decode, prefill and FP8-prefill token counts, and a tiny case
+#: for the oracle on every token.
+FFN_WORKLOADS = {
+    "dense_tiny_fp32": FfnShape("dense_tiny_fp32", tokens=40, dim=256, inter=384, dtype="f32"),
+    "dense_decode_bf16": FfnShape("dense_decode_bf16", tokens=16, dim=7168, inter=18432, dtype="bf16"),
+    "dense_prefill_bf16": FfnShape("dense_prefill_bf16", tokens=4096, dim=7168, inter=18432, dtype="bf16"),
+    "dense_prefill_fp8": FfnShape("dense_prefill_fp8", tokens=16384, dim=7168, inter=18432, dtype="fp8"),
+}
+
+_FFN_TID = dict(x=21, w1=22, w3=23, w2=24)
+
+
+@dataclass
+class FfnTensors:
+    """Device (or host) tensors of one dense feed-forward workload. Scales are None unless fp8."""
+
+    shape: FfnShape
+    x: torch.Tensor
+    w1: torch.Tensor
+    w3: torch.Tensor
+    w2: torch.Tensor
+    s1: Optional[torch.Tensor] = None
+    s3: Optional[torch.Tensor] = None
+    s2: Optional[torch.Tensor] = None
+
+
+def generate_ffn(shape: FfnShape, seed: int = 0, device="cpu") -> FfnTensors:
+    """x ~ N(0, 1) in the activation dtype; w1, w3 [I, D] ~ N(0, 1/D), w2 [D, I] ~ N(0, 1/I), in the
+    storage dtype (fp8: e4m3fn codes with one fp32 scale per 128x128 block, as for the experts)."""
+    device = torch.device(device)
+    t, d, i = shape.tokens, shape.dim, shape.inter
+    act = torch.float32 if shape.dtype == "f32" else torch.bfloat16
+    x = torch.randn(t, d, generator=_gen(device, seed, _FFN_TID["x"]), device=device, dtype=torch.float32).to(act)
+    w1, s1 = _matrix(shape, seed, _FFN_TID["w1"], 0, i, d, d, device)
+    w3, s3 = _matrix(shape, seed, _FFN_TID["w3"], 0, i, d, d, device)
+    w2, s2 = _matrix(shape, seed, _FFN_TID["w2"], 0, d, i, i, device)
+    return FfnTensors(shape, x, w1, w3, w2, s1, s3, s2)

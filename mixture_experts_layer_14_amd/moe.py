@@ -12,7 +12,7 @@ from typing import Optional
 
 import torch
 
-from .inputs import MoeShape, MoeTensors
+from .inputs import FfnShape, FfnTensors, MoeShape, MoeTensors
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 _lib = None
@@ -26,7 +26,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_CONFIG", -3: "MOE_ERR_WOR
 #: Every function include/moe.h declares.
 EXPORTS = ["moe_workspace_size", "moe_route", "moe_dispatch", "moe_forward", "moe_workspace_layout",
            "moe_status_str", "moe_last_error", "moe_timing_enable", "moe_timing_filter",
-           "moe_timing_report"]
+           "moe_timing_report", "moe_ffn_workspace_size", "moe_ffn"]
 
 
 class MoeConfig(ctypes.Structure):
@@ -45,6 +45,14 @@ class MoeWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ["idx", "w", "counts", "offsets", "row_token", "row_of", "h_routed", "h_shared", "h_scale",
                  "h_shared_scale", "o_routed", "o_shared", "xq", "x_scale", "total"]]
+
+
+class FfnConfig(ctypes.Structure):
+    _fields_ = [("dim", ctypes.c_int32), ("inter", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class FfnWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ["w1", "w3", "w2", "s1", "s3", "s2"]]
 
 
 class MoeError(RuntimeError):
@@ -66,7 +74,10 @@ def lib() -> ctypes.CDLL:
         L.moe_route.argtypes = [ctypes.POINTER(MoeConfig), vp, vp, vp, i64, vp, vp, vp, sz, vp]
         L.moe_dispatch.argtypes = [ctypes.POINTER(MoeConfig), vp, i64, vp, vp, vp, vp, vp, sz, vp]
         L.moe_forward.argtypes = [ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeWeights), vp, i64, vp, vp, sz, vp]
-        for f in ["moe_workspace_size", "moe_workspace_layout", "moe_route", "moe_dispatch", "moe_forward"]:
+        L.moe_ffn_workspace_size.argtypes = [ctypes.POINTER(FfnConfig), i64, ctypes.POINTER(sz)]
+        L.moe_ffn.argtypes = [ctypes.POINTER(FfnConfig), ctypes.POINTER(FfnWeights), vp, i64, vp, vp, sz, vp]
+        for f in ["moe_workspace_size", "moe_workspace_layout", "moe_route", "moe_dispatch", "moe_forward",
+                  "moe_ffn_workspace_size", "moe_ffn"]:
             getattr(L, f).restype = ctypes.c_int
         L.moe_status_str.argtypes = [ctypes.c_int]
         L.moe_status_str.restype = ctypes.c_char_p
@@ -136,6 +147,26 @@ def forward(cfg: MoeConfig, wts: MoeWeights, x, out, ws, stream=None, tokens: Op
                              ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
 
 
+def ffn_config(shape: FfnShape) -> FfnConfig:
+    return FfnConfig(shape.dim, shape.inter, _DTYPE[shape.dtype])
+
+
+def ffn_weights(t: FfnTensors) -> FfnWeights:
+    return FfnWeights(*[_ptr(getattr(t, n)) for n in ["w1", "w3", "w2", "s1", "s3", "s2"]])
+
+
+def ffn_workspace_size(cfg: FfnConfig, tokens: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_ffn_workspace_size(ctypes.byref(cfg), tokens, ctypes.byref(n)), "moe_ffn_workspace_size")
+    return n.value
+
+
+def ffn(cfg: FfnConfig, wts: FfnWeights, x, out, ws, stream=None, tokens: Optional[int] = None):
+    n = x.shape[0] if tokens is None else tokens
+    _check(lib().moe_ffn(ctypes.byref(cfg), ctypes.byref(wts), _ptr(x), n, _ptr(out), _ptr(ws),
+                         ws.numel() * ws.element_size(), _stream(stream)), "moe_ffn")
+
+
 def timing_enable(on: bool):
     _check(lib().moe_timing_enable(1 if on else 0), "moe_timing_enable")
 
@@ -185,3 +216,24 @@ class Block:
         off = getattr(self.layout(tokens), name)
         nbytes = count * torch.empty((), dtype=dtype).element_size()
         return self.ws[off:off + nbytes].view(dtype)
+
+
+@dataclass
+class Ffn:
+    """The dense feed-forward of the first layers on the GPU: weights, a workspace sized for up to
+    `max_tokens`, and forward()."""
+
+    tensors: FfnTensors
+    max_tokens: int
+
+    def __post_init__(self):
+        self.cfg = ffn_config(self.tensors.shape)
+        self.wts = ffn_weights(self.tensors)
+        dev = self.tensors.x.device
+        self.ws = torch.empty(max(ffn_workspace_size(self.cfg, self.max_tokens), 1), dtype=torch.uint8, device=dev)
+
+    def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty_like(x)
+        ffn(self.cfg, self.wts, x, out, self.ws, stream)
+        return out

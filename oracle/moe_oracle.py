@@ -16,6 +16,11 @@ Plain, slow, obviously-correct numpy in float64, written from two pages:
     expert on every token) and the parameter table (three 7168x2048 matrices per
     expert).
 
+  * "Hardware for DeepSeek-V3 and R1: Why a 671B MoE Model Needs So Much
+    Memory", section "Why the dense layers and shared expert matter": the first
+    three layers are ordinary dense feed-forward blocks with an intermediate
+    size of 18,432 (dense_ffn).
+
 Readings where the pages are silent (each is listed in the design notes):
   R1  the linear of the router has no bias; its dot product is exact (fp64
       sum of exact bf16 / fp32 products) and rounded once to fp32.
@@ -38,6 +43,9 @@ Readings where the pages are silent (each is listed in the design notes):
       token's experts divided by their sum, in fp64, rounded once to fp32; the
       gathered softmax scores are not renormalised (the excerpt renormalises
       only the sigmoid branch) before the route scale.
+  R11 the dense feed-forward is the MLP the MoE block page uses for its shared
+      expert (same R6 form, same R7 roundings), applied to every token; no
+      router, no weighting, its output row is the result.
 
 Functions and their pins (tests/test_oracle_*.py):
   bf16 / e4m3 codecs      torch's bfloat16 / float8_e4m3fn casts; spec values
@@ -57,6 +65,10 @@ Functions and their pins (tests/test_oracle_*.py):
   moe_forward             dense-G formulation bit-exact; x=0; W2 doubling;
                           token-permutation equivariance; E=K=1 reduces to
                           2.5 * MLP + shared MLP
+  dense_ffn               equals the block with one expert, K = 1, scale 1 and
+                          a zero shared down projection, bit for bit;
+                          torch.nn.functional MLP; 1x1 closed form (silu on the
+                          W1 branch); x = 0; W2 doubling; token permutation
 Full-shape output values have no printed example on the pages: beyond the
 pins above they are parity unpinned.
 """
@@ -414,6 +426,14 @@ def moe_forward_dense(cfg, x: np.ndarray, w_gate: np.ndarray, bias: Optional[np.
     w1, w3, w2 = shared()
     y = (y + swiglu_rows(xa, w1, w3, w2, act, out_dtype)).astype(f32)
     return y if out_dtype == "f32" else round_bf16(y)
+
+
+def dense_ffn(x: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray, act: str,
+              out_dtype: str) -> np.ndarray:
+    """The first layers' dense feed-forward (R11) on tokens x [T, D] (exact input values): the
+    image of x the GEMMs read (R9 for fp8), then w2( silu(w1 x) * (w3 x) ) with the R7 roundings.
+    w1, w3 [I, D], w2 [D, I] fp64 ([out, in]). Returns the rows in x's dtype as fp32 values."""
+    return swiglu_rows(activation_input(x, act), w1, w3, w2, act, out_dtype)
 
 
 def param_count(dim: int, n_experts: int, inter: int, n_shared: int, bias: bool = True) -> dict:

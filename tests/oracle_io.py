@@ -52,3 +52,18 @@ def oracle_forward(tens, x=None):
     act, out = act_out(tens.shape)
     xx = exact(tens.x) if x is None else x
     return O.moe_forward(tens.shape, xx, exact(tens.w_gate), bias_np(tens), expert, shared, act, out)
+
+
+def ffn_mats(tens):
+    """fp64 [out, in] weights of a dense feed-forward workload (fp8: dequantised blocks)."""
+    if tens.shape.dtype == "fp8":
+        return tuple(O.dequant_128x128(codes(w), s.detach().cpu().numpy())
+                     for w, s in ((tens.w1, tens.s1), (tens.w3, tens.s3), (tens.w2, tens.s2)))
+    return exact(tens.w1), exact(tens.w3), exact(tens.w2)
+
+
+def oracle_ffn(tens, x=None, mats=None):
+    """Run the oracle's dense feed-forward on tens (optionally on tokens x [n, D] fp64)."""
+    w1, w3, w2 = ffn_mats(tens) if mats is None else mats
+    act, out = act_out(tens.shape)
+    return O.dense_ffn(exact(tens.x) if x is None else x, w1, w3, w2, act, out)

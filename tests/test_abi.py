@@ -104,3 +104,53 @@ def test_forward_host_checks_without_gpu():
     assert L.moe_forward(ctypes.byref(cfg8), ctypes.byref(w), 0x1000, 16, 0x2000, 0x3000, 1 << 40, None) == -1
     # null weights struct
     assert L.moe_forward(ctypes.byref(cfg), None, 0x1000, 16, 0x2000, 0x3000, 1 << 40, None) == -1
+
+
+def ffn_size(shape, T):
+    n = ctypes.c_size_t()
+    cfg = moe.ffn_config(shape)
+    return moe.lib().moe_ffn_workspace_size(ctypes.byref(cfg), T, ctypes.byref(n)), n.value
+
+
+def test_ffn_workspace_size():
+    """The dense feed-forward's workspace holds h [T, inter] in the activation dtype (+ x's e4m3 image
+    and the scales for fp8), and grows with T; the output is written in place of o_shared."""
+    sh = inputs.FFN_WORKLOADS["dense_prefill_bf16"]
+    st, n = ffn_size(sh, 4096)
+    assert st == 0 and 4096 * 18432 * 2 <= n < 4096 * 18432 * 2 + (1 << 20)
+    st16, n16 = ffn_size(sh, 16)
+    assert st16 == 0 and n16 < n
+    st8, n8 = ffn_size(inputs.FFN_WORKLOADS["dense_prefill_fp8"], 16384)
+    assert st8 == 0 and n8 >= 16384 * (18432 + 7168 + (18432 + 7168) // 128 * 4)
+    assert ffn_size(sh, 0) == (0, ffn_size(sh, 0)[1])
+
+
+@pytest.mark.parametrize("dim,inter,dtype,code", [
+    (7000, 18432, "bf16", -5),   # dim not a multiple of 128
+    (7168, 100, "bf16", -5),     # inter not a multiple of 32
+    (7168, 18400, "fp8", -5),    # inter not a multiple of 128 for fp8
+    (0, 18432, "bf16", -2),
+    (256, 384, "f64", None),     # unknown dtype (checked below)
+])
+def test_ffn_bad_configs_rejected(dim, inter, dtype, code):
+    if dtype == "f64":
+        cfg = moe.FfnConfig(256, 384, 7)
+        n = ctypes.c_size_t()
+        assert moe.lib().moe_ffn_workspace_size(ctypes.byref(cfg), 4, ctypes.byref(n)) == -2
+        return
+    st, _ = ffn_size(inputs.FfnShape("bad", 4, dim, inter, dtype), 4)
+    assert st == code
+    assert moe.lib().moe_last_error() != b""
+
+
+def test_ffn_host_checks_without_gpu():
+    L = moe.lib()
+    cfg = moe.ffn_config(inputs.FFN_WORKLOADS["dense_decode_bf16"])
+    w = moe.FfnWeights(0x1000, 0x1000, 0x1000, None, None, None)
+    assert L.moe_ffn(ctypes.byref(cfg), ctypes.byref(w), 0x1000, 0, 0x2000, None, 0, None) == 0   # T = 0
+    assert L.moe_ffn(ctypes.byref(cfg), ctypes.byref(w), 0x1000, 16, 0x2000, 0x3000, 10, None) == -3
+    assert L.moe_ffn(ctypes.byref(cfg), ctypes.byref(w), 0x1004, 16, 0x2000, 0x3000, 1 << 40, None) == -1
+    assert L.moe_ffn(ctypes.byref(cfg), None, 0x1000, 16, 0x2000, 0x3000, 1 << 40, None) == -1
+    assert L.moe_ffn(ctypes.byref(cfg), ctypes.byref(w), 0x1000, -1, 0x2000, 0x3000, 1 << 40, None) == -1
+    cfg8 = moe.ffn_config(inputs.FFN_WORKLOADS["dense_prefill_fp8"])
+    assert L.moe_ffn(ctypes.byref(cfg8), ctypes.byref(w), 0x1000, 16, 0x2000, 0x3000, 1 << 40, None) == -1

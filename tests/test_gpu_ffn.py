@@ -1,0 +1,105 @@
+"""Parity of the dense feed-forward (moe_ffn, through the C ABI) with the CPU oracle.
+
+Small shapes are checked on every token at token counts that take each kernel path (16-row
+stream / fp8 kernels below 64 tokens, the weight-stream, ring and 128-row kernels above) with
+ragged tails; the DeepSeek-V3 dense layer (dim 7168, intermediate 18,432) is checked at the
+decode, prefill and FP8-prefill token counts on every token (decode) or sampled tokens."""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_14_amd import inputs, moe
+from tests.oracle_io import exact, ffn_mats, oracle_ffn
+from tests.parity import out_check, say, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+F = inputs.FfnShape
+
+SMALL = {
+    "dense_tiny_fp32": inputs.FFN_WORKLOADS["dense_tiny_fp32"],
+    # bf16: weight-stream kernels (dim % 256, inter % 256), the ring kernels (inter % 128), the
+    # 128-row kernels (dim % 128, inter % 64)
+    "dense_wstream_bf16": F("dense_wstream_bf16", tokens=300, dim=512, inter=1536, dtype="bf16"),
+    "dense_ring_bf16": F("dense_ring_bf16", tokens=300, dim=512, inter=1408, dtype="bf16"),
+    "dense_wide_bf16": F("dense_wide_bf16", tokens=300, dim=384, inter=1472, dtype="bf16"),
+    # fp8: weight-stream kernels (dim, inter % 512) and the 128-row kernels
+    "dense_wstream_fp8": F("dense_wstream_fp8", tokens=300, dim=1024, inter=1536, dtype="fp8"),
+    "dense_wide_fp8": F("dense_wide_fp8", tokens=300, dim=512, inter=640, dtype="fp8"),
+}
+FULL = ["dense_decode_bf16", "dense_prefill_bf16", "dense_prefill_fp8"]
+
+
+def run_ffn(tens, tokens):
+    blk = moe.Ffn(tens, max(tokens, 1))
+    out = blk.forward(tens.x[:tokens])
+    torch.cuda.synchronize()
+    return blk, out
+
+
+@pytest.mark.parametrize("name,T", [(n, t) for n in SMALL for t in (1, 16, 63, 64, 129, 300)])
+def test_ffn_small_all_tokens(name, T):
+    shape = SMALL[name].with_tokens(T)
+    say(f"[ffn/small] {name} T={T} D={shape.dim} I={shape.inter} dtype={shape.dtype}")
+    tens = inputs.generate_ffn(shape, seed=0, device=DEV)
+    _, out = run_ffn(tens, T)
+    rep = out_check(shape, to_np(out), oracle_ffn(tens))
+    say(f"  out {rep}")
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_ffn_full_shape(name):
+    shape = inputs.FFN_WORKLOADS[name]
+    T = shape.tokens
+    say(f"[ffn/full] {name} T={T} D={shape.dim} I={shape.inter} dtype={shape.dtype}: generating weights")
+    tens = inputs.generate_ffn(shape, seed=0, device=DEV)
+    _, out = run_ffn(tens, T)
+    rng = np.random.default_rng(1)
+    sample = np.arange(T) if T <= 16 else np.unique(np.concatenate([[0, T - 1], rng.choice(T, 10, replace=False)]))
+    say(f"  oracle on {len(sample)} tokens")
+    want = oracle_ffn(tens, x=exact(tens.x)[sample], mats=ffn_mats(tens))
+    rep = out_check(shape, to_np(out)[sample], want)
+    say(f"  out {rep}")
+
+
+def test_ffn_zero_tokens_is_noop():
+    tens = inputs.generate_ffn(SMALL["dense_wstream_bf16"].with_tokens(4), seed=0, device=DEV)
+    blk = moe.Ffn(tens, 4)
+    out = torch.full_like(tens.x, 7.0)
+    moe.ffn(blk.cfg, blk.wts, tens.x, out, blk.ws, tokens=0)
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
+
+
+@pytest.mark.parametrize("name", ["dense_wstream_bf16", "dense_wstream_fp8"])
+def test_ffn_deterministic_reruns(name):
+    tens = inputs.generate_ffn(SMALL[name], seed=3, device=DEV)
+    blk, a = run_ffn(tens, tens.shape.tokens)
+    b = blk.forward(tens.x)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_ffn_graph_replay_matches_eager():
+    """The dense feed-forward captured in a HIP graph replays to the eager result, with eager
+    launches and synchronisations between the replays."""
+    tens = inputs.generate_ffn(SMALL["dense_wstream_fp8"], seed=7, device=DEV)
+    blk = moe.Ffn(tens, tens.shape.tokens)
+    ref = blk.forward(tens.x).clone()
+    out = torch.empty_like(ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        blk.forward(tens.x, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        blk.forward(tens.x, out)
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        blk.forward(tens.x)
+        torch.cuda.synchronize()
