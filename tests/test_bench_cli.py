@@ -8,7 +8,8 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
-import bench  # noqa: E402
+import bench
+from mixture_experts_layer_14_amd import inputs  # noqa: E402
 
 
 def test_more_than_one_gpu_is_refused_before_touching_a_device():
@@ -42,7 +43,7 @@ def test_committed_traffic_entries_are_well_formed():
     assert recs
     for key, rec in recs.items():
         workload, kernel = key.split(":", 1)
-        assert workload in ("decode_bf16", "prefill_bf16", "skewed_bf16", "prefill_fp8")
+        assert workload in inputs.WORKLOADS or workload in inputs.FFN_WORKLOADS
         assert rec["bytes_per_launch"] > 0
         assert abs(rec["fetch_scale"] - 2.0) < 0.01 and abs(rec["write_scale"] - 1.0) < 0.01
         assert len(rec["source_hash"]) == 16
