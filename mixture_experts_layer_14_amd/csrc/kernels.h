@@ -139,13 +139,15 @@ struct WideItem {
 };
 
 // item -> (tile, n-tile): routed items first (per_r n-tiles per expert), then the shared
-// expert's (per_s). Within an expert the M-tiles go in ceil(mt / kGroupM) groups of nearly equal
-// size (at most kGroupM, the first mt % groups one larger); a group's items run n-tile by n-tile,
-// its M-tiles adjacent within an n-tile. Blocks that run together on one XCD (32 consecutive
-// items) then share each weight tile among the group's M-tiles and each activation tile among
-// the n-tiles in flight (8 x 4 for a large expert: 256 KB of distinct operands per k-step
-// instead of 544 KB for 32 M-tiles of one n-tile). An expert of at most kGroupM M-tiles is one
-// group, in the plain order.
+// expert's (per_s). Within an expert the M-tiles go in round(mt / kGroupM) groups of nearly equal
+// size (the first mt % groups one larger); a group's items run n-tile by n-tile, its M-tiles
+// adjacent within an n-tile. Blocks that run together on one XCD (32 consecutive items) then
+// share each weight tile among the group's M-tiles and each activation tile among the n-tiles in
+// flight. With G M-tiles per group an expert's operand traffic goes as weights / G +
+// activations * G / 32, weight tiles being twice the bytes of an activation tile: least at
+// G = 8 (a large expert then moves 256 KB of distinct operands per k-step instead of 544 KB for
+// 32 M-tiles of one n-tile), within 4% for 6 to 11. An expert of up to 11 M-tiles stays one group
+// in the plain order.
 constexpr int kGroupM = 8;
 template <int BM = kWideBM>
 MOE_DEV WideItem wide_item(int item, const Tile* __restrict__ tiles, int nr, const int32_t* __restrict__ offsets,
@@ -163,7 +165,7 @@ MOE_DEV WideItem wide_item(int item, const Tile* __restrict__ tiles, int nr, con
   const int rows = probe.expert == E ? T : offsets[probe.expert + 1] - offsets[probe.expert];
   const int mt = (rows + BM - 1) / BM;
   const int local = local_item - (first - base_tiles) * per;
-  const int ng = (mt + kGroupM - 1) / kGroupM;
+  const int ng = max(1, (mt + kGroupM / 2) / kGroupM);
   const int base = mt / ng, big = mt % ng;  // groups 0 .. big-1 hold base + 1 M-tiles, the rest base
   const int split = big * (base + 1) * per;  // first item of the smaller groups
   int g, gsz, rem;

@@ -21,7 +21,8 @@ Plain, slow, obviously-correct numpy in float64, written from two pages:
     three layers are ordinary dense feed-forward blocks with an intermediate
     size of 18,432 (dense_ffn).
 
-Readings where the pages are silent (each is listed in the design notes):
+Readings where the pages are silent (numbered as in the design notes, where R10-R12 and
+R14 concern the ABI and the test rules):
   R1  the linear of the router has no bias; its dot product is exact (fp64
       sum of exact bf16 / fp32 products) and rounded once to fp32.
   R2  sigmoid evaluated in fp64, rounded once to fp32.
@@ -39,11 +40,11 @@ Readings where the pages are silent (each is listed in the design notes):
       cast to x's dtype.
   R9  FP8 (OCP e4m3fn, bias 7, max 448, no infinities): scale = amax / 448
       (1 when amax = 0), code = round-to-nearest-even(v / scale), saturating.
-  R10 softmax scoring (the excerpt's other branch): exp(z - max z) over the
+  R13 softmax scoring (the excerpt's other branch): exp(z - max z) over the
       token's experts divided by their sum, in fp64, rounded once to fp32; the
       gathered softmax scores are not renormalised (the excerpt renormalises
       only the sigmoid branch) before the route scale.
-  R11 the dense feed-forward is the MLP the MoE block page uses for its shared
+  R15 the dense feed-forward is the MLP the MoE block page uses for its shared
       expert (same R6 form, same R7 roundings), applied to every token; no
       router, no weighting, its output row is the result.
 
@@ -430,7 +431,7 @@ def moe_forward_dense(cfg, x: np.ndarray, w_gate: np.ndarray, bias: Optional[np.
 
 def dense_ffn(x: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray, act: str,
               out_dtype: str) -> np.ndarray:
-    """The first layers' dense feed-forward (R11) on tokens x [T, D] (exact input values): the
+    """The first layers' dense feed-forward (R15) on tokens x [T, D] (exact input values): the
     image of x the GEMMs read (R9 for fp8), then w2( silu(w1 x) * (w3 x) ) with the R7 roundings.
     w1, w3 [I, D], w2 [D, I] fp64 ([out, in]). Returns the rows in x's dtype as fp32 values."""
     return swiglu_rows(activation_input(x, act), w1, w3, w2, act, out_dtype)

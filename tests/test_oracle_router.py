@@ -215,7 +215,7 @@ def test_dispatch_vs_lexsort(t, e, k):
             assert row_token[row] == tt and offsets[idx[tt, j]] <= row < offsets[idx[tt, j] + 1]
 
 
-# ---- softmax scoring (the Gate.forward excerpt's softmax branch; reading R10)
+# ---- softmax scoring (the Gate.forward excerpt's softmax branch; reading R13)
 def scfg(**kw):
     c = cfg(**kw)
     c.score_func = "softmax"
