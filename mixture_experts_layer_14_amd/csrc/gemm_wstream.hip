@@ -56,7 +56,7 @@ MOE_DEV f32x16 mfma32w(i32x4 a, i32x4 b, f32x16 c) {
                                                  0, 0, 0);
 }
 
-// NT: weight loads nontemporal
+// NT: every weight load nontemporal (else only the gate/up tiles of single-M-tile experts)
 template <int MODE, bool NT>
 __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
     const bf16_t* __restrict__ act_x, const bf16_t* __restrict__ h_routed_in, const bf16_t* __restrict__ h_shared_in,
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
   auto item_of = [&](int i) __attribute__((always_inline)) {
     WsItem d;
     d.live = i < mine;
-    d.row0 = 0, d.nrows = 0, d.nt = 0, d.expert = 0, d.rot = 0, d.sh = false;
+    d.row0 = 0, d.nrows = 0, d.nt = 0, d.expert = 0, d.rot = 0, d.sh = false, d.solo = false;
     if (d.live) {
       const WideItem it = wide_item<WS_BM>(xcd * chunk + slot + i * per_xcd, tiles, nr, offsets, T, E, per_r, per_s);
       d.row0 = it.tl.row0;
@@ -92,6 +92,7 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
       d.nt = it.nt;
       d.expert = it.tl.expert;
       d.sh = it.shared;
+      d.solo = it.mt == 1;
       // each item starts its k walk at its own step, so concurrent items spread over the HBM channels
       d.rot = (MODE == 0 ? 3 * d.expert : 3 * d.expert + 5 * d.nt) % nk;
     }
@@ -114,6 +115,7 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
   // slab rows 8 i .. 8 i + 7 (mode 0: W1 rows for i < 4, the W3 rows of the same columns after)
   __amdgpu_buffer_rsrc_t br0, br1;
   int b_row8, b_rot, b_voff[4];
+  bool b_solo = false;
   auto b_set = [&](const WsItem& d) __attribute__((always_inline)) {
     int ldb;
     if (MODE == 0) {
@@ -128,6 +130,7 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
     }
     b_row8 = __builtin_amdgcn_readfirstlane(8 * ldb);
     b_rot = d.rot;
+    b_solo = d.solo;
     const int ln = lane_now();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -137,9 +140,16 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
   auto issue_b = [&](int slot_b, int ks) __attribute__((always_inline)) {
     const int kb = kbytes(ks, b_rot);
     char* dst = wslab + slot_b * WS_SLAB;
+    // gate/up weight tiles of a single-M-tile expert are read by one item only: nontemporal, so they
+    // do not push out of L2 the tiles that other M-tiles of an expert are about to read
+    if (MODE == 0 && b_solo) {
 #pragma unroll
-    for (int i = 0; i < WS_BQ; ++i)
-      ws_dma<NT>(MODE == 0 && i >= 4 ? br1 : br0, dst + i * 1024, b_voff[i & 3], kb + (MODE == 0 ? (i & 3) : i) * b_row8);
+      for (int i = 0; i < WS_BQ; ++i) ws_dma<true>(i >= 4 ? br1 : br0, dst + i * 1024, b_voff[i & 3], kb + (i & 3) * b_row8);
+    } else {
+#pragma unroll
+      for (int i = 0; i < WS_BQ; ++i)
+        ws_dma<NT>(MODE == 0 && i >= 4 ? br1 : br0, dst + i * 1024, b_voff[i & 3], kb + (MODE == 0 ? (i & 3) : i) * b_row8);
+    }
   };
 
   // ---- activation rows: instruction q of this wave fills tile rows 32 wave + 8 q + lane / 8

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(64 * WQ_WAVES) void gemm_wstream_fp8(
   auto item_of = [&](int i) __attribute__((always_inline)) {
     WsItem d;
     d.live = i < mine;
-    d.row0 = 0, d.nrows = 0, d.nt = 0, d.expert = 0, d.rot = 0, d.sh = false;
+    d.row0 = 0, d.nrows = 0, d.nt = 0, d.expert = 0, d.rot = 0, d.sh = false, d.solo = false;
     if (d.live) {
       const WideItem it = wide_item<WQ_BM>(xcd * chunk + slot + i * per_xcd, tiles, nr, offsets, T, E, per_r, per_s);
       d.row0 = it.tl.row0;

@@ -30,6 +30,7 @@ MOE_DEV void ws_dma(__amdgpu_buffer_rsrc_t r, char* lds_dst, int voff, int soff)
 struct WsItem {  // one work item of a block (wave-uniform)
   int row0, nrows, nt, expert, rot;
   bool sh, live;
+  bool solo;  // the item's expert has a single M-tile: no other item reads its weight tiles
 };
 
 }  // namespace moe
