@@ -56,7 +56,7 @@ MOE_DEV f32x16 mfma32w(i32x4 a, i32x4 b, f32x16 c) {
                                                  0, 0, 0);
 }
 
-// NT: every weight load nontemporal (else only the gate/up tiles of single-M-tile experts)
+// NT: every weight load nontemporal (else only the tiles of single-M-tile experts)
 template <int MODE, bool NT>
 __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
     const bf16_t* __restrict__ act_x, const bf16_t* __restrict__ h_routed_in, const bf16_t* __restrict__ h_shared_in,
@@ -140,11 +140,12 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
   auto issue_b = [&](int slot_b, int ks) __attribute__((always_inline)) {
     const int kb = kbytes(ks, b_rot);
     char* dst = wslab + slot_b * WS_SLAB;
-    // gate/up weight tiles of a single-M-tile expert are read by one item only: nontemporal, so they
-    // do not push out of L2 the tiles that other M-tiles of an expert are about to read
-    if (MODE == 0 && b_solo) {
+    // weight tiles of a single-M-tile expert are read by one item only: nontemporal, so they do not
+    // push out of L2 the tiles that other M-tiles of an expert are about to read
+    if (b_solo) {
 #pragma unroll
-      for (int i = 0; i < WS_BQ; ++i) ws_dma<true>(i >= 4 ? br1 : br0, dst + i * 1024, b_voff[i & 3], kb + (i & 3) * b_row8);
+      for (int i = 0; i < WS_BQ; ++i)
+        ws_dma<true>(MODE == 0 && i >= 4 ? br1 : br0, dst + i * 1024, b_voff[i & 3], kb + (MODE == 0 ? (i & 3) : i) * b_row8);
     } else {
 #pragma unroll
       for (int i = 0; i < WS_BQ; ++i)
