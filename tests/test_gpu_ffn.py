@@ -28,6 +28,9 @@ SMALL = {
     "dense_wide_fp8": F("dense_wide_fp8", tokens=300, dim=512, inter=640, dtype="fp8"),
 }
 FULL = ["dense_decode_bf16", "dense_prefill_bf16", "dense_prefill_fp8"]
+# 13 M-tiles of 128 rows: two groups (7 + 6) in the grouped item order, every token checked
+GROUPED = [F("dense_grouped_bf16", tokens=1664, dim=256, inter=512, dtype="bf16"),
+           F("dense_grouped_fp8", tokens=1664, dim=512, inter=512, dtype="fp8")]
 
 
 def run_ffn(tens, tokens):
@@ -45,6 +48,14 @@ def test_ffn_small_all_tokens(name, T):
     _, out = run_ffn(tens, T)
     rep = out_check(shape, to_np(out), oracle_ffn(tens))
     say(f"  out {rep}")
+
+
+@pytest.mark.parametrize("shape", GROUPED, ids=lambda s: s.name)
+def test_ffn_grouped_order_all_tokens(shape):
+    say(f"[ffn/grouped] {shape.name} T={shape.tokens}")
+    tens = inputs.generate_ffn(shape, seed=5, device=DEV)
+    _, out = run_ffn(tens, shape.tokens)
+    say(f"  out {out_check(shape, to_np(out), oracle_ffn(tens))}")
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -33,6 +33,12 @@ SMALL = {
                      inter=512, n_shared=1, route_scale=2.5, dtype="fp8", hot_bias=0.5),
     "wstream_fp8_long": S("wstream_fp8_long", tokens=300, dim=2048, n_experts=8, n_groups=2, topk_groups=1,
                           topk=2, inter=1024, n_shared=1, route_scale=2.5, dtype="fp8"),
+    # experts of 12+ M-tiles and a 24-tile shared expert: the grouped item order of the 128-row
+    # kernels (groups of 6 to 11 M-tiles), checked on every token
+    "big_expert_bf16": S("big_expert_bf16", tokens=3000, dim=256, n_experts=2, n_groups=1, topk_groups=1, topk=1,
+                         inter=256, n_shared=1, route_scale=1.0, dtype="bf16"),
+    "big_expert_fp8": S("big_expert_fp8", tokens=3000, dim=512, n_experts=2, n_groups=1, topk_groups=1, topk=1,
+                        inter=512, n_shared=1, route_scale=1.0, dtype="fp8"),
     "wide_bf16": S("wide_bf16", tokens=700, dim=768, n_experts=16, n_groups=4, topk_groups=2, topk=4, inter=256,
                    n_shared=1, route_scale=2.5, dtype="bf16", hot_bias=0.5),
     # more experts than threads in a block: several experts per router thread
