@@ -212,6 +212,35 @@ void drop_spans() {
 }  // namespace
 
 namespace moe {
+int device_lds_limit() {
+  static std::mutex mu;
+  static std::map<int, int> cache;  // device -> per-block LDS limit
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) v = 0;
+  cache[dev] = v;
+  return v;
+}
+
+hipError_t allow_dynamic_lds(const void* kernel, size_t bytes) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, hipError_t> done;  // (device, kernel) -> result
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  auto key = std::make_pair(dev, kernel);
+  auto it = done.find(key);
+  if (it != done.end()) return it->second;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  done[key] = e;
+  return e;
+}
+
 int persistent_grid(const void* kernel, int threads, size_t dyn_lds, int max_per_cu) {
   static std::mutex mu;
   static std::map<std::pair<int, const void*>, std::pair<int, int>> cache;  // (blocks per CU, CUs)

@@ -206,14 +206,7 @@ constexpr int RBM = MOE_RING_BM, RBN = MOE_RING_BN, RBK = MOE_RING_BK, RST = MOE
 static size_t ring_lds() { return (size_t)RST * (RBM + RBN) * RBK * 2; }
 
 bool ring_ok(const Dims& d) {
-  static int lds_max = -1;  // per-block LDS limit of the device
-  if (lds_max < 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-      v = 0;
-    lds_max = v;
-  }
+  const int lds_max = device_lds_limit();
   return d.dtype == 1 && ring_lds() <= (size_t)lds_max && d.D % RBN == 0 && d.I % (RBN / 2) == 0 &&
          d.S % (RBN / 2) == 0 && d.I % RBK == 0 && d.S % RBK == 0;
 }
@@ -222,11 +215,8 @@ hipError_t launch_ring_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hi
   const size_t lds = ring_lds();
   const void* k0 = (const void*)gemm_ring_bf16<0, RBM, RBN, RBK, RST>;
   const void* k1 = (const void*)gemm_ring_bf16<1, RBM, RBN, RBK, RST>;
-  static const hipError_t attr = [&] {
-    hipError_t e = hipFuncSetAttribute(k0, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e == hipSuccess) e = hipFuncSetAttribute(k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    return e;
-  }();
+  hipError_t attr = allow_dynamic_lds(k0, lds);
+  if (attr == hipSuccess) attr = allow_dynamic_lds(k1, lds);
   if (attr != hipSuccess) return attr;  // never launch with more LDS than the kernel may take
   const Tile* tiles = RBM == kWideBM2 ? a.tiles_wide2 : a.tiles_wide;
   const int g0 = persistent_grid(k0, 64 * R_WAVES, lds) & ~7;

@@ -325,14 +325,7 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
 }
 
 bool wstream_ok(const Dims& d) {
-  static int lds_max = -1;  // per-block LDS limit of the device
-  if (lds_max < 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-      v = 0;
-    lds_max = v;
-  }
+  const int lds_max = device_lds_limit();
   const int64_t lim = WS_RANGE - (1 << 20);
   return d.dtype == 1 && WS_LDS <= (size_t)lds_max && d.D % 256 == 0 && d.I % 256 == 0 && d.S == d.I &&
          d.T * d.D * 2 < lim && d.R * d.I * 2 < lim && d.T * d.S * 2 < lim;
@@ -342,11 +335,8 @@ template <bool NT>
 static hipError_t launch_wstream_nt(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s) {
   const void* k0 = (const void*)gemm_wstream_bf16<0, NT>;
   const void* k1 = (const void*)gemm_wstream_bf16<1, NT>;
-  static const hipError_t attr = [&] {
-    hipError_t e = hipFuncSetAttribute(k0, hipFuncAttributeMaxDynamicSharedMemorySize, (int)WS_LDS);
-    if (e == hipSuccess) e = hipFuncSetAttribute(k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)WS_LDS);
-    return e;
-  }();
+  hipError_t attr = allow_dynamic_lds(k0, WS_LDS);
+  if (attr == hipSuccess) attr = allow_dynamic_lds(k1, WS_LDS);
   if (attr != hipSuccess) return attr;  // never launch with more LDS than the kernel may take
   const int g0 = persistent_grid(k0, 64 * WS_WAVES, WS_LDS) & ~7;
   const int g1 = persistent_grid(k1, 64 * WS_WAVES, WS_LDS) & ~7;

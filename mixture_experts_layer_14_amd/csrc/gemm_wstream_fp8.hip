@@ -388,14 +388,7 @@ __global__ __launch_bounds__(64 * WQ_WAVES) void gemm_wstream_fp8(
 }
 
 bool wstream_fp8_ok(const Dims& d) {
-  static int lds_max = -1;  // per-block LDS limit of the device
-  if (lds_max < 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-      v = 0;
-    lds_max = v;
-  }
+  const int lds_max = device_lds_limit();
   const int64_t lim = WS_RANGE - (1 << 20);
   return d.dtype == 2 && WQ_LDS <= (size_t)lds_max && d.D % 512 == 0 && d.I % 512 == 0 && d.S == d.I &&
          d.T * d.D < lim && d.R * d.I < lim && d.T * d.S < lim && d.R * (d.I / 128) * 4 < lim &&
@@ -405,11 +398,8 @@ bool wstream_fp8_ok(const Dims& d) {
 hipError_t launch_wstream_fp8(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s) {
   const void* k0 = (const void*)gemm_wstream_fp8<0>;
   const void* k1 = (const void*)gemm_wstream_fp8<1>;
-  static const hipError_t attr = [&] {
-    hipError_t e = hipFuncSetAttribute(k0, hipFuncAttributeMaxDynamicSharedMemorySize, (int)WQ_LDS);
-    if (e == hipSuccess) e = hipFuncSetAttribute(k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)WQ_LDS);
-    return e;
-  }();
+  hipError_t attr = allow_dynamic_lds(k0, WQ_LDS);
+  if (attr == hipSuccess) attr = allow_dynamic_lds(k1, WQ_LDS);
   if (attr != hipSuccess) return attr;  // never launch with more LDS than the kernel may take
   const int g0 = persistent_grid(k0, 64 * WQ_WAVES, WQ_LDS) & ~7;
   const int g1 = persistent_grid(k1, 64 * WQ_WAVES, WQ_LDS) & ~7;

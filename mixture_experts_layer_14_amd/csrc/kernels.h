@@ -101,6 +101,10 @@ int dense_down_split(const Dims& d);
 // Blocks of `kernel` that fit on the current device at once (occupancy x CUs, the occupancy capped
 // at max_per_cu when that is positive), cached per device and kernel.
 int persistent_grid(const void* kernel, int threads, size_t dyn_lds = 0, int max_per_cu = 0);
+// The current device's per-block LDS limit (cached per device).
+int device_lds_limit();
+// Once per (device, kernel): let `kernel` take `bytes` of dynamic LDS; the result is cached.
+hipError_t allow_dynamic_lds(const void* kernel, size_t bytes);
 // 128-row LDS-tiled fp8 kernels with 128-k scale promotion (prefill-sized batches)
 bool wide_fp8_ok(const Dims& d);
 hipError_t launch_wide_fp8(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
