@@ -255,3 +255,39 @@ def test_graph_replay_matches_eager(name):
         assert torch.equal(out, ref)
         blk.forward(tens.x)  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["mid_bf16", "wstream_fp8"])
+def test_workspace_reuse_across_token_counts(name):
+    """One workspace, calls of 300, 17, 1 and again 300 tokens: every output equals the one a fresh
+    workspace gives (nothing of an earlier, larger call leaks through the tile lists or counters)."""
+    shape = SMALL[name]
+    tens = inputs.generate(shape.with_tokens(300), seed=11, device=DEV)
+    blk = moe.Block(tens, 300)
+    for t in (300, 17, 1, 300):
+        out = blk.forward(tens.x[:t])
+        fresh = moe.Block(tens, t).forward(tens.x[:t])
+        torch.cuda.synchronize()
+        assert torch.equal(out, fresh), t
+
+
+def test_two_streams_two_workspaces():
+    """Two blocks with their own workspaces running on two streams at once give the same outputs as
+    run one after the other (the library keeps no shared device state between calls)."""
+    sa, sb = SMALL["mid_bf16"], SMALL["wstream_fp8"]
+    ta = inputs.generate(sa, seed=12, device=DEV)
+    tb = inputs.generate(sb, seed=13, device=DEV)
+    ba, bb = moe.Block(ta, sa.tokens), moe.Block(tb, sb.tokens)
+    ref_a, ref_b = ba.forward(ta.x).clone(), bb.forward(tb.x).clone()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    oa, ob = torch.empty_like(ref_a), torch.empty_like(ref_b)
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            ba.forward(ta.x, oa)
+        with torch.cuda.stream(s2):
+            bb.forward(tb.x, ob)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ref_a) and torch.equal(ob, ref_b)
