@@ -19,11 +19,13 @@
 //     tile's end take an out-of-range offset and read as zeros without touching memory.
 //
 // Step n (64 k of one item): wait until this wave's part of activation stage n and its slab n
-// have landed, barrier (stage n is complete and every wave is done with stage n - 1), request
-// activation stage n + 3 and slab n + 2, multiply. Vector-memory loads complete in issue order,
-// so each step issues the activation loads (short latency) before the weight loads, and the wait
-// at step n leaves stage n + 2 and slab n + 1 in flight. The step sequence runs on across the
-// block's items without draining: an item's last steps request the next item's first stages.
+// have landed, barrier (stage n is complete and every wave is done with stage n - 1), multiply,
+// and request activation stage n + 3 and slab n + 2 between the MFMAs of the step's four k-steps
+// (issued in one burst before them, the twelve loads held up the MFMAs: 3% slower). Vector-memory
+// loads complete in issue order, so each step issues the activation loads (short latency) before
+// the weight loads, and the wait at step n leaves stage n + 2 and slab n + 1 in flight. The step
+// sequence runs on across the block's items without draining: an item's last steps request the
+// next item's first stages. A ragged tile multiplies only its live 32-row groups.
 //
 // Steps come in groups of four (the activation stages rotate with the group), so an item's steps
 // (dim / 64 or inter / 64) must be a multiple of four; the epilogue and the accumulator reset run
@@ -137,20 +139,25 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
       b_voff[i] = d.live ? (ln >> 3) * ldb + ((((ln & 7) ^ (ln >> 3)) ^ i) << 4) : WS_OOB;
   };
   char* const wslab = lds + WS_B0 + wave * (WS_NB * WS_SLAB);  // this wave's three slabs
-  auto issue_b = [&](int slot_b, int ks) __attribute__((always_inline)) {
+  // instructions I0 .. I1 - 1 of the slab
+  auto issue_b = [&](auto i0, auto i1, int slot_b, int ks) __attribute__((always_inline)) {
+    constexpr int I0 = decltype(i0)::value, I1 = decltype(i1)::value;
     const int kb = kbytes(ks, b_rot);
     char* dst = wslab + slot_b * WS_SLAB;
     // weight tiles of a single-M-tile expert are read by one item only: nontemporal, so they do not
     // push out of L2 the tiles that other M-tiles of an expert are about to read
     if (b_solo) {
 #pragma unroll
-      for (int i = 0; i < WS_BQ; ++i)
+      for (int i = I0; i < I1; ++i)
         ws_dma<true>(MODE == 0 && i >= 4 ? br1 : br0, dst + i * 1024, b_voff[i & 3], kb + (MODE == 0 ? (i & 3) : i) * b_row8);
     } else {
 #pragma unroll
-      for (int i = 0; i < WS_BQ; ++i)
+      for (int i = I0; i < I1; ++i)
         ws_dma<NT>(MODE == 0 && i >= 4 ? br1 : br0, dst + i * 1024, b_voff[i & 3], kb + (MODE == 0 ? (i & 3) : i) * b_row8);
     }
+  };
+  auto issue_b_all = [&](int slot_b, int ks) __attribute__((always_inline)) {
+    issue_b(std::integral_constant<int, 0>{}, std::integral_constant<int, WS_BQ>{}, slot_b, ks);
   };
 
   // ---- activation rows: instruction q of this wave fills tile rows 32 wave + 8 q + lane / 8
@@ -202,7 +209,9 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
   for (int kk = 0; kk < WS_BK / 16; ++kk) foff[kk] = ws_pos(l32, kk * 2 + lh);
   // Fragments of k-step kk + 1 are read while the MFMAs of kk run (two register sets); the
   // scheduling groups spread those reads between the MFMAs.
-  auto compute = [&](auto nm, int stage, int slot_b) __attribute__((always_inline)) {
+  // issue(kk) runs after the MFMAs of k-step kk: the step's loads go out between its MFMAs
+  // instead of in one burst before them.
+  auto compute = [&](auto nm, int stage, int slot_b, auto&& issue) __attribute__((always_inline)) {
     constexpr int NM = decltype(nm)::value;
     constexpr int KK = WS_BK / 16;
     const char* As = lds + stage * WS_A_STAGE;
@@ -225,6 +234,7 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
         acc[m][0] = mfma32w(fa[cb][m], fb[cb][0], acc[m][0]);
         acc[m][1] = mfma32w(fa[cb][m], fb[cb][1], acc[m][1]);
       }
+      issue(kk);
       if (kk + 1 < KK) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
 #pragma unroll
@@ -265,36 +275,40 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
   // Step j of a group (j = 0..3, step n = 4 g + j of the item, its slab in slot sb): multiply
   // stage j with slab n, request stage n + 3 (into stage (j + 3) % 4, at a_ks of the activation
   // cursor's item) and slab n + 2 (into slot (sb + 2) % 3, at b_ks of the weight cursor's item).
+  // Only the item's live 32-row groups (nm of them) are multiplied; the loads do not depend on nm.
   int sb = 0;  // slot of slab n
-  auto step = [&](int j, int a_ks, int b_ks) __attribute__((always_inline)) {
+  auto step = [&](auto nm, int j, int a_ks, int b_ks) __attribute__((always_inline)) {
     wait_vmcnt<WS_AQ + WS_BQ>();  // loads after slab n: stage n + 2, slab n + 1
     wait_lgkm0();
     barrier_only();
-    issue_a((j + 3) & 3, a_ks);
-    issue_b(sb == 0 ? 2 : sb - 1, b_ks);
-    compute(std::integral_constant<int, WS_NM>{}, j, sb);
+    const int sbn = sb == 0 ? 2 : sb - 1;
+    compute(nm, j, sb, [&](int kk) __attribute__((always_inline)) {
+      using std::integral_constant;
+      if (kk == 0) issue_a((j + 3) & 3, a_ks);
+      if (kk == 1) issue_b(integral_constant<int, 0>{}, integral_constant<int, 3>{}, sbn, b_ks);
+      if (kk == 2) issue_b(integral_constant<int, 3>{}, integral_constant<int, 6>{}, sbn, b_ks);
+      if (kk == 3) issue_b(integral_constant<int, 6>{}, integral_constant<int, WS_BQ>{}, sbn, b_ks);
+    });
     sb = sb == 2 ? 0 : sb + 1;
   };
-  // the non-final groups of an item: both cursors stay inside the item
-  auto body = [&]() __attribute__((always_inline)) {
+  // One item's steps: the non-final groups (both cursors stay inside the item), then the final
+  // group, in which the activation cursor moves to the next item after the first step and the
+  // weight cursor after the second.
+  auto run_item = [&](auto nm, const WsItem& next) __attribute__((always_inline)) {
     for (int g = 0; g < nk / 4 - 1; ++g) {
       const int k0 = 4 * g;
-      step(0, k0 + 3, k0 + 2);
-      step(1, k0 + 4, k0 + 3);
-      step(2, k0 + 5, k0 + 4);
-      step(3, k0 + 6, k0 + 5);
+      step(nm, 0, k0 + 3, k0 + 2);
+      step(nm, 1, k0 + 4, k0 + 3);
+      step(nm, 2, k0 + 5, k0 + 4);
+      step(nm, 3, k0 + 6, k0 + 5);
     }
-  };
-  // the final group: the activation cursor moves to the next item after the first step, the
-  // weight cursor after the second
-  auto tail = [&](const WsItem& next) __attribute__((always_inline)) {
     const int tok_next = tok_load(next);
-    step(0, nk - 1, nk - 2);
+    step(nm, 0, nk - 1, nk - 2);
     a_set(next, tok_next);
-    step(1, 0, nk - 1);
+    step(nm, 1, 0, nk - 1);
     b_set(next);
-    step(2, 1, 0);
-    step(3, 2, 1);
+    step(nm, 2, 1, 0);
+    step(nm, 3, 2, 1);
   };
 
   // prologue, in the issue order of the steps before step 0: stage 0; stage 1, slab 0; stage 2, slab 1
@@ -304,9 +318,9 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
   wait_vmcnt<0>();
   issue_a(0, 0);
   issue_a(1, 1);
-  issue_b(0, 0);
+  issue_b_all(0, 0);
   issue_a(2, 2);
-  issue_b(1, 1);
+  issue_b_all(1, 1);
 
   for (int i = 0; i < mine; ++i) {
 #pragma unroll
@@ -316,8 +330,17 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[m][t][q] = 0.f;
     const WsItem next = item_of(i + 1);
-    body();
-    tail(next);
+    // a ragged tile multiplies only its live row groups (one code path per count, so the step
+    // loop itself has no branches)
+    const int nm = __builtin_amdgcn_readfirstlane(min(WS_NM, (cur.nrows + 31) >> 5));
+    if (nm >= 4)
+      run_item(std::integral_constant<int, 4>{}, next);
+    else if (nm == 3)
+      run_item(std::integral_constant<int, 3>{}, next);
+    else if (nm == 2)
+      run_item(std::integral_constant<int, 2>{}, next);
+    else
+      run_item(std::integral_constant<int, 1>{}, next);
     epilogue(cur);
     cur = next;
   }

@@ -21,11 +21,12 @@
 // scale and one FMA per element, and the other wave of the SIMD issues MFMAs meanwhile.
 //
 // Step n: wait until this wave's part of stage n and its slab n have landed, barrier (stage n is
-// complete and every wave is done with stage n - 1), request stage and slab n + 2, multiply.
-// Loads complete in issue order, so activations, row scales and weights of a step are issued
-// together and the wait at step n leaves stage and slab n + 1 in flight. The step sequence runs
-// on across the block's items; steps come in groups of four, so dim / 128 and inter / 128 must be
-// multiples of four.
+// complete and every wave is done with stage n - 1), multiply, and request stage and slab n + 2
+// one or two loads after each row group's MFMAs (issued in one burst before the MFMAs, the loads
+// held them up: 13% slower). Loads complete in issue order, so activations, row scales and weights
+// of a step all go out within the step and the wait at step n leaves stage and slab n + 1 in
+// flight. The step sequence runs on across the block's items; steps come in groups of four, so
+// dim / 128 and inter / 128 must be multiples of four.
 #include <type_traits>
 
 #include "wstream.h"
@@ -141,11 +142,13 @@ __global__ __launch_bounds__(64 * WQ_WAVES) void gemm_wstream_fp8(
       b_voff[i] = d.live ? (ln >> 3) * ldb + ((((ln & 7) ^ (ln >> 3)) ^ i) << 4) : WS_OOB;
   };
   char* const wslab = lds + WQ_B0 + wave * (WQ_NS * WQ_SLAB);  // this wave's three slabs
-  auto issue_b = [&](int slot_b, int ks) __attribute__((always_inline)) {
+  // instructions I0 .. I1 - 1 of the slab
+  auto issue_b = [&](auto i0, auto i1, int slot_b, int ks) __attribute__((always_inline)) {
+    constexpr int I0 = decltype(i0)::value, I1 = decltype(i1)::value;
     const int kb = blk(ks, b_rot) * 128;
     char* dst = wslab + slot_b * WQ_SLAB;
 #pragma unroll
-    for (int i = 0; i < WQ_BQ; ++i)
+    for (int i = I0; i < I1; ++i)
       ws_dma<false>(MODE == 0 && i >= 2 ? br1 : br0, dst + i * 1024, b_voff[i],
                     kb + (MODE == 0 ? (i & 1) : i) * b_row8);
   };
@@ -196,6 +199,9 @@ __global__ __launch_bounds__(64 * WQ_WAVES) void gemm_wstream_fp8(
     char* dst = lds + stage * WQ_A + wave * WQ_AQ * 1024;
 #pragma unroll
     for (int q = 0; q < WQ_AQ; ++q) ws_dma<false>(r, dst + q * 1024, a_voff[q], kbi * 128);
+  };
+  auto issue_s = [&](int stage, int ks) __attribute__((always_inline)) {  // the stage's row scales
+    const int kbi = blk(ks, a_rot);
     const __amdgpu_buffer_rsrc_t rs = ws_rsrc(s_base, WS_RANGE);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rs, (__attribute__((address_space(3))) void*)(lds + WQ_SX0 + stage * WQ_SX + wave * 256), 4, s_voff, kbi * 4, 0,
@@ -213,7 +219,9 @@ __global__ __launch_bounds__(64 * WQ_WAVES) void gemm_wstream_fp8(
 #pragma unroll
     for (int h = 0; h < 2; ++h) foff[kk][h] = ws_pos(l32, kk * 4 + lh * 2 + h);
   const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int st, float sw0, float sw1) __attribute__((always_inline)) {
+  // issue(m) runs after the MFMAs of row group m: the step's loads go out between its MFMAs
+  // instead of in one burst before them.
+  auto compute = [&](int st, float sw0, float sw1, auto&& issue) __attribute__((always_inline)) {
     const char* As = lds + st * WQ_A;
     const char* Bs = wslab + st * WQ_SLAB;
     // tile row 32 m + l32's scale: wave m's area holds rows 32 m .. 32 m + 31
@@ -232,6 +240,7 @@ __global__ __launch_bounds__(64 * WQ_WAVES) void gemm_wstream_fp8(
 #pragma unroll
     for (int m = 0; m < WQ_NM; ++m) {
       p[m & 1] = mfma32q(b1, a1, mfma32q(b0, a0, zero16));
+      issue(m);
       const float sx_m = sx;
       if (m + 1 < WQ_NM) {  // next group's rows and scale; read after the MFMAs that use a0 / a1
         a0 = ws_frag32(As + (m + 1) * 4096, foff[0][0], foff[0][1]);
@@ -331,10 +340,17 @@ __global__ __launch_bounds__(64 * WQ_WAVES) void gemm_wstream_fp8(
     wait_lgkm0();
     barrier_only();
     const int s2 = st == 0 ? 2 : st - 1;
-    issue_a(s2, ks);
-    issue_b(s2, ks);
     const int kbc = blk(ks_c, c_rot);
-    compute(st, wsc0[kbc], wsc1[kbc]);
+    compute(st, wsc0[kbc], wsc1[kbc], [&](int m) __attribute__((always_inline)) {
+      using std::integral_constant;
+      if (m == 0) issue_a(s2, ks);
+      if (m == 1) {
+        issue_s(s2, ks);
+        issue_b(integral_constant<int, 0>{}, integral_constant<int, 1>{}, s2, ks);
+      }
+      if (m == 2) issue_b(integral_constant<int, 1>{}, integral_constant<int, 3>{}, s2, ks);
+      if (m == 3) issue_b(integral_constant<int, 3>{}, integral_constant<int, WQ_BQ>{}, s2, ks);
+    });
     st = st == 2 ? 0 : st + 1;
   };
   auto body = [&]() __attribute__((always_inline)) {
@@ -362,10 +378,13 @@ __global__ __launch_bounds__(64 * WQ_WAVES) void gemm_wstream_fp8(
   b_set(cur);
   a_set(cur, tok_load(cur));
   wait_vmcnt<0>();
+  using std::integral_constant;
   issue_a(0, 0);
-  issue_b(0, 0);
+  issue_s(0, 0);
+  issue_b(integral_constant<int, 0>{}, integral_constant<int, WQ_BQ>{}, 0, 0);
   issue_a(1, 1);
-  issue_b(1, 1);
+  issue_s(1, 1);
+  issue_b(integral_constant<int, 0>{}, integral_constant<int, WQ_BQ>{}, 1, 1);
 
   for (int i = 0; i < mine; ++i) {
 #pragma unroll
