@@ -2,7 +2,8 @@
 
 Small shapes are checked on every token at token counts that take each kernel path (16-row
 stream / fp8 kernels below 64 tokens, the weight-stream, ring and 128-row kernels above) with
-ragged tails; the DeepSeek-V3 dense layer (dim 7168, intermediate 18,432) is checked at the
+ragged tails whose last 128-row tile has 1, 2, 3 or 4 live 32-row groups (129, 64 / 300, 96 / 200,
+128 tokens); the DeepSeek-V3 dense layer (dim 7168, intermediate 18,432) is checked at the
 decode, prefill and FP8-prefill token counts on every token (decode) or sampled tokens."""
 import numpy as np
 import pytest
@@ -40,7 +41,7 @@ def run_ffn(tens, tokens):
     return blk, out
 
 
-@pytest.mark.parametrize("name,T", [(n, t) for n in SMALL for t in (1, 16, 63, 64, 129, 300)])
+@pytest.mark.parametrize("name,T", [(n, t) for n in SMALL for t in (1, 16, 63, 64, 96, 129, 200, 300)])
 def test_ffn_small_all_tokens(name, T):
     shape = SMALL[name].with_tokens(T)
     say(f"[ffn/small] {name} T={T} D={shape.dim} I={shape.inter} dtype={shape.dtype}")
