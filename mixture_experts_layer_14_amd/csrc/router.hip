@@ -497,6 +497,9 @@ hipError_t launch_router_logits(const Dims& d, const void* x, const void* w_gate
 hipError_t launch_router_select(const Dims& d, const double* zpart, int nsplit, const float* bias,
                                 float route_scale, bool softmax, int32_t* idx, float* w, hipStream_t s) {
   if (d.T == 0) return hipSuccess;
+  // the selection kernel's per-token arrays are sized for these limits (the ABI rejects larger
+  // configurations before any launch)
+  if (d.E > kMaxE || d.G > kMaxG || d.K > kMaxK || nsplit > kMaxSplit) return hipErrorInvalidValue;
   // one token per block for small batches (latency), one per wave for large ones with E <= 256
 #define MOE_SELECT(EPT, TPB)                                                                              \
   MOE_LAUNCH((router_select<EPT, TPB>), dim3((unsigned)((d.T + TPB - 1) / TPB)), dim3(256), 0, s, zpart, nsplit, \
