@@ -123,6 +123,33 @@ def test_forward_full_shape(name):
         say(f"  fraction of assignments on the 32 biased experts: {hot:.4f}")
 
 
+def test_forward_beyond_2gb_activations():
+    """152,000 tokens of the full bf16 block: x alone is 2.18 GB, past the 2 GB byte range of the
+    weight-stream kernels' buffer resources, so the 256-row ring kernels take the expert GEMMs
+    (1.2 M routed rows, 17 GB of expert outputs). Routing and dispatch on every token, outputs on
+    sampled tokens."""
+    shape = inputs.WORKLOADS["prefill_bf16"].with_tokens(152_000)
+    T = shape.tokens
+    assert T * shape.dim * 2 > 2 ** 31
+    say(f"[forward/beyond 2 GB] T={T}: generating weights")
+    tens = inputs.generate(shape, seed=4, device=DEV)
+    say("  running the block")
+    blk, out = run_block(tens)
+    say("  oracle routing on every token")
+    xe = exact(tens.x)
+    r = O.route(shape, xe, exact(tens.w_gate), bias_np(tens))
+    gidx, gw = gpu_route(blk, shape, T)
+    bad, rep = route_check(shape, r, gidx, gw)
+    say(f"  route {rep}")
+    dispatch_check(shape, gidx, *gpu_dispatch(blk, shape, T))
+    rng = np.random.default_rng(4)
+    sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 8, replace=False)]))
+    say(f"  oracle forward on {len(sample)} tokens")
+    f = oracle_forward(tens, x=xe[sample])
+    got = to_np(out[torch.as_tensor(sample, device=out.device)])
+    say(f"  out {out_check(shape, got, f.out, skip=bad[sample])}")
+
+
 @pytest.mark.parametrize("name,T", [("mid_bf16", 1), ("mid_bf16", 17), ("mid_bf16", 64), ("mid_fp8", 3),
                                     ("mid_fp8", 40), ("mid_fp8", 129), ("wstream_fp8", 64),
                                     ("wstream_fp8", 257)])
