@@ -123,15 +123,16 @@ def test_forward_full_shape(name):
         say(f"  fraction of assignments on the 32 biased experts: {hot:.4f}")
 
 
-def test_forward_beyond_2gb_activations():
-    """152,000 tokens of the full bf16 block: x alone is 2.18 GB, past the 2 GB byte range of the
-    weight-stream kernels' buffer resources, so the 256-row ring kernels take the expert GEMMs
-    (1.2 M routed rows, 17 GB of expert outputs). Routing and dispatch on every token, outputs on
-    sampled tokens."""
-    shape = inputs.WORKLOADS["prefill_bf16"].with_tokens(152_000)
-    T = shape.tokens
-    assert T * shape.dim * 2 > 2 ** 31
-    say(f"[forward/beyond 2 GB] T={T}: generating weights")
+@pytest.mark.parametrize("name,T", [("prefill_bf16", 152_000), ("prefill_fp8", 300_000)])
+def test_forward_beyond_2gb_activations(name, T):
+    """The full block with activations past the 2 GB byte range of the weight-stream kernels'
+    buffer resources: bf16 at 152,000 tokens (x is 2.18 GB; the 256-row ring kernels take the
+    expert GEMMs, 1.2 M routed rows, 17 GB of expert outputs), fp8 at 300,000 tokens (x's e4m3
+    image is 2.15 GB; the 128-row fp8 kernels take them, 34 GB of expert outputs). Routing and
+    dispatch on every token, outputs on sampled tokens."""
+    shape = inputs.WORKLOADS[name].with_tokens(T)
+    assert T * shape.dim * (2 if shape.dtype == "bf16" else 1) > 2 ** 31
+    say(f"[forward/beyond 2 GB] {name} T={T}: generating weights")
     tens = inputs.generate(shape, seed=4, device=DEV)
     say("  running the block")
     blk, out = run_block(tens)
