@@ -74,6 +74,23 @@ def test_ffn_full_shape(name):
     say(f"  out {rep}")
 
 
+@pytest.mark.parametrize("name,T", [("dense_prefill_bf16", 60_000), ("dense_prefill_fp8", 120_000)])
+def test_ffn_beyond_2gb_activations(name, T):
+    """The 18,432-wide layer with h [T, 18432] past the 2 GB byte range of the weight-stream
+    kernels' buffer resources (bf16 h 2.21 GB at 60,000 tokens: the ring kernels run; fp8 h 2.21 GB
+    at 120,000 tokens: the 128-row fp8 kernels run), sampled tokens against the oracle."""
+    shape = inputs.FFN_WORKLOADS[name].with_tokens(T)
+    assert T * shape.inter * (2 if shape.dtype == "bf16" else 1) > 2 ** 31
+    say(f"[ffn/beyond 2 GB] {name} T={T}: generating weights")
+    tens = inputs.generate_ffn(shape, seed=4, device=DEV)
+    _, out = run_ffn(tens, T)
+    rng = np.random.default_rng(4)
+    sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 8, replace=False)]))
+    want = oracle_ffn(tens, x=exact(tens.x[torch.as_tensor(sample, device=tens.x.device)]), mats=ffn_mats(tens))
+    got = to_np(out[torch.as_tensor(sample, device=out.device)])
+    say(f"  out {out_check(shape, got, want)}")
+
+
 def test_ffn_zero_tokens_is_noop():
     tens = inputs.generate_ffn(SMALL["dense_wstream_bf16"].with_tokens(4), seed=0, device=DEV)
     blk = moe.Ffn(tens, 4)
