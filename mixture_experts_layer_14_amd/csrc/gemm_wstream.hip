@@ -13,8 +13,9 @@
 // each lane fetches the 16-byte chunk that belongs at its slot under the swizzle below):
 //   weights, read once from HBM: a wave-private ring of three 64-k slabs (64 rows x 128 bytes; one
 //     instruction reads 8 rows x 128 contiguous bytes), two slabs in flight while the third is
-//     multiplied: 64 KB of weights in flight per CU. Loads are nontemporal when the batch's
-//     experts mostly fit one M-tile, so that each weight tile is read by one item only.
+//     multiplied: 64 KB of weights in flight per CU. The weight loads of an expert with a single
+//     M-tile are nontemporal (no other item reads those tiles), and so are all weight loads when
+//     the routed experts average less than one M-tile.
 //   activation rows (small, L2-resident): a 4-stage ring shared by the block; rows past the
 //     tile's end take an out-of-range offset and read as zeros without touching memory.
 //
