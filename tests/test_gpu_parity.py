@@ -27,6 +27,10 @@ SMALL = {
                           inter=96, n_shared=2, route_scale=2.5, dtype="bf16", hot_bias=0.5),
     "mid_fp8": S("mid_fp8", tokens=200, dim=1024, n_experts=32, n_groups=4, topk_groups=2, topk=6, inter=256,
                  n_shared=1, route_scale=2.5, dtype="fp8"),
+    # two shared experts (hidden 2 * inter) in fp8: the 128-row fp8 kernels (the weight-stream ones
+    # need the shared hidden size equal to inter), skewed routing with ragged tiles
+    "mid_fp8_shared2": S("mid_fp8_shared2", tokens=300, dim=512, n_experts=16, n_groups=4, topk_groups=2, topk=4,
+                         inter=512, n_shared=2, route_scale=2.5, dtype="fp8", hot_bias=0.5),
     # the fp8 weight-stream GEMMs (dim and inter multiples of 512): skewed routing gives experts of
     # several M-tiles, ragged tails and empty experts; the second shape runs the k loop's body
     "wstream_fp8": S("wstream_fp8", tokens=600, dim=1024, n_experts=16, n_groups=4, topk_groups=2, topk=4,
