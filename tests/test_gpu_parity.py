@@ -247,6 +247,35 @@ def test_fp8_activation_codes_bit_exact():
     assert np.array_equal(O.e4m3_decode(xq), O.e4m3_decode(q))
 
 
+def test_fp8_special_blocks():
+    """Planted 1x128 blocks: token 0 all zeros (every x and h block has amax 0, so scale 1 and zero
+    codes; its output is exactly zero), token 1 one zero block and one block scaled to about 1e3,
+    token 2 a single non-zero value. Codes and scales bit-exact, the output within the fp8
+    tolerance."""
+    shape = SMALL["mid_fp8"]
+    tens = inputs.generate(shape, seed=9, device=DEV)
+    x = tens.x
+    x[0] = 0
+    x[1, :128] = 0
+    x[1, 256:384] = (x[1, 256:384].float() * 1000).to(x.dtype)
+    x[2] = 0
+    x[2, 700] = 3.0
+    blk, out = run_block(tens)
+    T, D = shape.tokens, shape.dim
+    xq = blk.ws_view(T, "xq", torch.uint8, T * D).view(T, D).cpu().numpy()
+    sx = blk.ws_view(T, "x_scale", torch.float32, T * D // 128).view(T, D // 128).cpu().numpy()
+    q, sc = O.quant_1x128(exact(x).astype(np.float32))
+    assert np.array_equal(sx, sc) and (sx[0] == 1.0).all() and sx[1, 0] == 1.0
+    assert np.array_equal(O.e4m3_decode(xq), O.e4m3_decode(q))
+    assert (xq[0] & 0x7F == 0).all()
+    f = oracle_forward(tens)
+    gidx, gw = gpu_route(blk, shape, T)
+    bad, _ = route_check(shape, f.route, gidx, gw)
+    got = to_np(out)
+    assert (got[0] == 0).all()
+    out_check(shape, got, f.out, skip=bad)
+
+
 @pytest.mark.parametrize("name", ["mid_bf16", "mid_fp8", "wstream_fp8"])
 def test_deterministic_reruns(name):
     shape = SMALL[name]
