@@ -127,6 +127,21 @@ def test_forward_full_shape(name):
         say(f"  fraction of assignments on the 32 biased experts: {hot:.4f}")
 
 
+@pytest.mark.parametrize("name", ["decode_bf16", "prefill_fp8"])
+def test_forward_full_shape_single_token(name):
+    """One token through the full block (batch-1 decode): nine expert M-tiles of one row each on the
+    16-row paths (bf16 stream kernels; fp8 16-row kernels), every value checked."""
+    shape = inputs.WORKLOADS[name].with_tokens(1)
+    say(f"[forward/full, 1 token] {name}")
+    tens = inputs.generate(shape, seed=8, device=DEV)
+    blk, out = run_block(tens)
+    f = oracle_forward(tens)
+    gidx, gw = gpu_route(blk, shape, 1)
+    bad, rep = route_check(shape, f.route, gidx, gw)
+    dispatch_check(shape, gidx, *gpu_dispatch(blk, shape, 1))
+    say(f"  route {rep}\n  out {out_check(shape, to_np(out), f.out, skip=bad)}")
+
+
 @pytest.mark.parametrize("name,T", [("prefill_bf16", 152_000), ("prefill_fp8", 300_000)])
 def test_forward_beyond_2gb_activations(name, T):
     """The full block with activations past the 2 GB byte range of the weight-stream kernels'
