@@ -127,6 +127,25 @@ def test_forward_full_shape(name):
         say(f"  fraction of assignments on the 32 biased experts: {hot:.4f}")
 
 
+@pytest.mark.parametrize("T", [16, 4096])
+def test_forward_full_shape_softmax(T):
+    """Softmax scoring (the Gate.forward branch DeepSeek-V3 does not use) on the full bf16 block:
+    a 256-thread block per token at 16 tokens, a wave per token at 4096. Routing on every token,
+    outputs on sampled tokens."""
+    shape = inputs.WORKLOADS["prefill_bf16"].replace(name="softmax_full_bf16", tokens=T, score_func="softmax")
+    say(f"[forward/full softmax] T={T}")
+    tens = inputs.generate(shape, seed=10, device=DEV)
+    blk, out = run_block(tens)
+    r = O.route(shape, exact(tens.x), exact(tens.w_gate), bias_np(tens))
+    gidx, gw = gpu_route(blk, shape, T)
+    bad, rep = route_check(shape, r, gidx, gw)
+    dispatch_check(shape, gidx, *gpu_dispatch(blk, shape, T))
+    sample = np.arange(T) if T <= 16 else np.unique(np.concatenate([[0, T - 1],
+                                                                    np.random.default_rng(10).choice(T, 8, replace=False)]))
+    f = oracle_forward(tens, x=exact(tens.x)[sample])
+    say(f"  route {rep}\n  out {out_check(shape, to_np(out)[sample], f.out, skip=bad[sample])}")
+
+
 @pytest.mark.parametrize("name", ["decode_bf16", "prefill_fp8"])
 def test_forward_full_shape_single_token(name):
     """One token through the full block (batch-1 decode): nine expert M-tiles of one row each on the
