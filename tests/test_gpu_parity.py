@@ -127,13 +127,15 @@ def test_forward_full_shape(name):
         say(f"  fraction of assignments on the 32 biased experts: {hot:.4f}")
 
 
-@pytest.mark.parametrize("T", [16, 4096])
-def test_forward_full_shape_softmax(T):
-    """Softmax scoring (the Gate.forward branch DeepSeek-V3 does not use) on the full bf16 block:
-    a 256-thread block per token at 16 tokens, a wave per token at 4096. Routing on every token,
-    outputs on sampled tokens."""
-    shape = inputs.WORKLOADS["prefill_bf16"].replace(name="softmax_full_bf16", tokens=T, score_func="softmax")
-    say(f"[forward/full softmax] T={T}")
+@pytest.mark.parametrize("T,score_func,has_bias", [(16, "softmax", True), (4096, "softmax", True),
+                                                   (4096, "sigmoid", False)])
+def test_forward_full_shape_router_variants(T, score_func, has_bias):
+    """The router branches DeepSeek-V3 does not use, on the full bf16 block: softmax scoring (a
+    256-thread block per token at 16 tokens, a wave per token at 4096) and no selection bias
+    (groups scored by their best expert). Routing on every token, outputs on sampled tokens."""
+    shape = inputs.WORKLOADS["prefill_bf16"].replace(name=f"{score_func}_full_bf16", tokens=T,
+                                                     score_func=score_func, has_bias=has_bias)
+    say(f"[forward/full router variant] T={T} {score_func} bias={has_bias}")
     tens = inputs.generate(shape, seed=10, device=DEV)
     blk, out = run_block(tens)
     r = O.route(shape, exact(tens.x), exact(tens.w_gate), bias_np(tens))
