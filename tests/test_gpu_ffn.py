@@ -74,6 +74,16 @@ def test_ffn_full_shape(name):
     say(f"  out {rep}")
 
 
+@pytest.mark.parametrize("name", ["dense_decode_bf16", "dense_prefill_fp8"])
+def test_ffn_full_width_single_token(name):
+    """One token through the 18,432-wide layer (the 16-row paths, every value)."""
+    shape = inputs.FFN_WORKLOADS[name].with_tokens(1)
+    say(f"[ffn/full, 1 token] {name}")
+    tens = inputs.generate_ffn(shape, seed=6, device=DEV)
+    _, out = run_ffn(tens, 1)
+    say(f"  out {out_check(shape, to_np(out), oracle_ffn(tens, mats=ffn_mats(tens)))}")
+
+
 @pytest.mark.parametrize("name,T", [("dense_prefill_bf16", 60_000), ("dense_prefill_fp8", 120_000)])
 def test_ffn_beyond_2gb_activations(name, T):
     """The 18,432-wide layer with h [T, 18432] past the 2 GB byte range of the weight-stream
