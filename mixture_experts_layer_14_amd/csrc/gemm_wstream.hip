@@ -21,12 +21,12 @@
 //
 // Step n (64 k of one item): wait until this wave's part of activation stage n and its slab n
 // have landed, barrier (stage n is complete and every wave is done with stage n - 1), multiply,
-// and request activation stage n + 3 and slab n + 2 between the MFMAs of the step's four k-steps
+// and request slab n + 2 and activation stage n + 3 between the MFMAs of the step's four k-steps
 // (issued in one burst before them, the twelve loads held up the MFMAs: 3% slower). Vector-memory
-// loads complete in issue order, so each step issues the activation loads (short latency) before
-// the weight loads, and the wait at step n leaves stage n + 2 and slab n + 1 in flight. The step
-// sequence runs on across the block's items without draining: an item's last steps request the
-// next item's first stages. A ragged tile multiplies only its live 32-row groups.
+// loads complete in issue order; each step issues its weight loads (HBM latency) before its
+// activation loads (L2 hits, needed three steps later), so the wait at step n leaves stage n + 1,
+// slab n + 1 and stage n + 2 in flight (activations first measured 1-2% slower). The step sequence runs on across the block's items without draining: an item's last
+// steps request the next item's first stages. A ragged tile multiplies only its live 32-row groups.
 //
 // Steps come in groups of four (the activation stages rotate with the group), so an item's steps
 // (dim / 64 or inter / 64) must be a multiple of four; the epilogue and the accumulator reset run
@@ -279,16 +279,16 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
   // Only the item's live 32-row groups (nm of them) are multiplied; the loads do not depend on nm.
   int sb = 0;  // slot of slab n
   auto step = [&](auto nm, int j, int a_ks, int b_ks) __attribute__((always_inline)) {
-    wait_vmcnt<WS_AQ + WS_BQ>();  // loads after slab n: stage n + 2, slab n + 1
+    wait_vmcnt<2 * WS_AQ + WS_BQ>();  // loads after slab n: stage n + 1, slab n + 1, stage n + 2
     wait_lgkm0();
     barrier_only();
     const int sbn = sb == 0 ? 2 : sb - 1;
     compute(nm, j, sb, [&](int kk) __attribute__((always_inline)) {
       using std::integral_constant;
-      if (kk == 0) issue_a((j + 3) & 3, a_ks);
-      if (kk == 1) issue_b(integral_constant<int, 0>{}, integral_constant<int, 3>{}, sbn, b_ks);
-      if (kk == 2) issue_b(integral_constant<int, 3>{}, integral_constant<int, 6>{}, sbn, b_ks);
-      if (kk == 3) issue_b(integral_constant<int, 6>{}, integral_constant<int, WS_BQ>{}, sbn, b_ks);
+      if (kk == 0) issue_b(integral_constant<int, 0>{}, integral_constant<int, 3>{}, sbn, b_ks);
+      if (kk == 1) issue_b(integral_constant<int, 3>{}, integral_constant<int, 6>{}, sbn, b_ks);
+      if (kk == 2) issue_b(integral_constant<int, 6>{}, integral_constant<int, WS_BQ>{}, sbn, b_ks);
+      if (kk == 3) issue_a((j + 3) & 3, a_ks);
     });
     sb = sb == 2 ? 0 : sb + 1;
   };
@@ -312,16 +312,17 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
     step(nm, 3, 2, 1);
   };
 
-  // prologue, in the issue order of the steps before step 0: stage 0; stage 1, slab 0; stage 2, slab 1
+  // prologue, in the issue order of the steps before step 0 (weights, then activations): stage 0; slab 0,
+  // stage 1; slab 1, stage 2
   WsItem cur = item_of(0);
   b_set(cur);
   a_set(cur, tok_load(cur));
   wait_vmcnt<0>();
   issue_a(0, 0);
-  issue_a(1, 1);
   issue_b_all(0, 0);
-  issue_a(2, 2);
+  issue_a(1, 1);
   issue_b_all(1, 1);
+  issue_a(2, 2);
 
   for (int i = 0; i < mine; ++i) {
 #pragma unroll
