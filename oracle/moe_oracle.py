@@ -4,17 +4,18 @@ TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, links or runs
 this file: only the tests, the smoke check and the bench's cpu_baseline leg
 do. It shares no code with the HIP kernels and imports nothing from them.
 
-Plain, slow, obviously-correct numpy in float64, written from two pages:
+Plain, slow, obviously-correct numpy in float64, written from three pages:
   * "DeepSeek-V3.2-Exp · Router" (atlas.klimoza.dev, router inspector): the four
     formula steps z = x W_r, s = sigma(z), E_sel = top-8 of (s + b) within the top
     4 groups, G_i = 2.5 s_i E_i / sum_j s_j E_j; and the Gate.forward excerpt
     (group view, top-2-sum group score, group mask, expert top-k, gather of the
     unbiased scores, renormalisation, route scale).
   * "DeepSeek-V3.2-Exp · Mixture of experts" (open-model-atlas, MoE block):
-    the MoE.forward excerpt (flatten tokens, fp32 accumulator, bincount, skip
-    empty experts, per-expert token gather in token order, weighted add, shared
-    expert on every token) and the parameter table (three 7168x2048 matrices per
-    expert).
+    the block's output, a per-token sum of the routed experts' outputs weighted
+    by the gate plus the shared expert's output, accumulated in fp32 in expert
+    order with the shared expert last (MoE.forward excerpt); the per-expert token
+    lists in token order (dispatch); the parameter table (three 7168x2048
+    matrices per expert).
 
   * "Hardware for DeepSeek-V3 and R1: Why a 671B MoE Model Needs So Much
     Memory", section "Why the dense layers and shared expert matter": the first
@@ -50,7 +51,13 @@ R14 concern the ABI and the test rules):
 
 Functions and their pins (tests/test_oracle_*.py):
   bf16 / e4m3 codecs      torch's bfloat16 / float8_e4m3fn casts; spec values
-  quant_1x128             amax maps to code 448; zero block; RNE error bound
+  quant_1x128             amax maps to code 448; zero block; RNE error bound;
+                          a hand-worked 1x128 row (exact codes, both tie cases,
+                          the smallest subnormal)
+  store_act("fp8")        torch's float8_e4m3fn cast of h / (amax / 448) per
+                          token per 128 columns, bit for bit, on a SwiGLU h
+                          written with torch.nn.functional; per-token scales
+                          (two tokens of different amax in one column block)
   router_logits           exact rational dot product (fractions) on tiny inputs;
                           identity router weight gives z = x
   sigmoid32               scipy.special.expit; sigma(0) = 0.5
@@ -62,7 +69,8 @@ Functions and their pins (tests/test_oracle_*.py):
                           <= 4 groups, sum 2.5); bias-shift invariance;
                           special cases G=1 / b=0 / E=K
   dispatch                lexsort of (expert, token) keys; permutation invariants
-  swiglu_rows             torch.nn.functional silu / linear in fp64
+  swiglu_rows             torch.nn.functional silu / linear in fp64 (f32, bf16,
+                          and fp8 with torch's float8 requantisation of h)
   moe_forward             dense-G formulation bit-exact; x=0; W2 doubling;
                           token-permutation equivariance; E=K=1 reduces to
                           2.5 * MLP + shared MLP
@@ -120,12 +128,18 @@ def _e4m3_table() -> np.ndarray:
 _E4M3_POS = _e4m3_table()
 
 
+def _e4m3_all() -> np.ndarray:
+    """Value of every e4m3fn code 0..255: the sign bit over the magnitude table; S.1111.111 is NaN."""
+    mag = np.concatenate([_E4M3_POS, [np.nan]])
+    return np.concatenate([mag, -mag])
+
+
+_E4M3_ALL = _e4m3_all()
+
+
 def e4m3_decode(codes: np.ndarray) -> np.ndarray:
-    """OCP e4m3fn codes (uint8) -> float64 values (NaN for S.1111.111)."""
-    c = np.asarray(codes, dtype=np.uint8)
-    mag = c & 0x7F
-    out = np.where(mag == 127, np.nan, _E4M3_POS[np.minimum(mag, 126)])
-    return np.where(c & 0x80, -out, out)
+    """OCP e4m3fn codes (uint8) -> float64 values (NaN for S.1111.111), by table lookup."""
+    return _E4M3_ALL[np.asarray(codes, dtype=np.uint8)]
 
 
 def e4m3_encode(v: np.ndarray) -> np.ndarray:
@@ -166,9 +180,9 @@ def dequant_1x128(codes: np.ndarray, scales: np.ndarray, block: int = 128) -> np
 def dequant_128x128(codes: np.ndarray, scales: np.ndarray, block: int = 128) -> np.ndarray:
     """e4m3 weight [R, C] with one scale per block x block tile -> float64 values."""
     r, c = codes.shape
-    v = e4m3_decode(codes).reshape(r // block, block, c // block, block)
-    v = v * scales.astype(f64)[:, None, :, None]
-    return v.reshape(r, c)
+    v = e4m3_decode(codes)
+    v.reshape(r // block, block, c // block, block)[...] *= scales.astype(f64)[:, None, :, None]
+    return v
 
 
 # --------------------------------------------------------------------------
@@ -386,28 +400,34 @@ def moe_forward(cfg, x: np.ndarray, w_gate: np.ndarray, bias: Optional[np.ndarra
                 act: str, out_dtype: str) -> Forward:
     """Delta [T, D] for tokens x [T, D] (exact input values).
 
+    The block's defining sum (router page, G_i; MoE block page, block output): per token,
+    Delta = sum over experts e ascending of G_e * FFN_e(x) + FFN_shared(x), where G_e is the
+    token's routing weight for e and zero for the experts it did not choose. A zero term adds an
+    exact zero to the fp32 accumulator, so only each expert's chosen tokens are evaluated: an
+    expert no token chose is never read. The dispatch permutation is computed on its own and
+    returned for the tests; the sum does not use it.
+
     expert(e) -> (w1, w3, w2) fp64 of routed expert e; shared() -> the shared expert's.
     act: activation storage dtype ("f32" | "bf16" | "fp8"); out_dtype: x's dtype."""
     x = np.asarray(x, f64)
     t, d = x.shape
     r = route(cfg, x, w_gate, bias)
-    counts, offsets, row_token, row_of = dispatch(r.idx, cfg.n_experts)
+    gate = dense_gate(r, cfg.n_experts)                # G [T, E]
+    chosen = np.zeros((t, cfg.n_experts), dtype=bool)
+    np.put_along_axis(chosen, r.idx.astype(np.int64), True, axis=1)
     xa = activation_input(x, act)
     y = np.zeros((t, d), dtype=f32)
-    for e in range(cfg.n_experts):            # routed experts, ascending
-        if counts[e] == 0:
-            continue                          # an expert with no tokens is never read
-        rows = np.arange(offsets[e], offsets[e + 1])
-        toks = row_token[rows]
-        ks = np.nonzero(r.idx[toks] == e)[1]  # each token lists e exactly once
-        wts = r.w[toks, ks]
+    for e in range(cfg.n_experts):                     # R8: ascending expert order
+        toks = np.nonzero(chosen[:, e])[0]
+        if toks.size == 0:
+            continue
         w1, w3, w2 = expert(e)
         o = swiglu_rows(xa[toks], w1, w3, w2, act, out_dtype)
-        y[toks] = (y[toks] + (o * wts[:, None]).astype(f32)).astype(f32)
+        y[toks] = (y[toks] + (o * gate[toks, e][:, None]).astype(f32)).astype(f32)
     w1, w3, w2 = shared()
     y = (y + swiglu_rows(xa, w1, w3, w2, act, out_dtype)).astype(f32)
     out = y if out_dtype == "f32" else round_bf16(y)
-    return Forward(out, r, (counts, offsets, row_token, row_of))
+    return Forward(out, r, dispatch(r.idx, cfg.n_experts))
 
 
 def moe_forward_dense(cfg, x: np.ndarray, w_gate: np.ndarray, bias: Optional[np.ndarray],
