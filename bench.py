@@ -11,9 +11,14 @@ Prints one JSON line: tokens/s, ms per step, the dominant kernel's roofline (alg
 flops per launch over its average duration, from HIP events around that kernel's launches inside
 the timed steps) and the CPU oracle timed on a bounded sample of the same workload. A pass of the
 same number of untimed steps before the timed ones, with events around every launch, gives the
-per-kernel breakdown (`kernels_ms`) and picks the dominant kernel.
+per-kernel breakdown (`kernels_ms`) and picks the dominant kernel. `step` puts the whole step
+against its roofs: algorithmic bytes over the HBM peak and flops over the MFMA peak.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+With the default decode headline, `workloads` adds the block's other workloads timed in the same
+run (tiny fp32, 4096-token bf16 prefill, skewed 4096-token prefill, 16384-token fp8 prefill), each
+with the same step and dominant-kernel figures.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-workloads]
 """
 from __future__ import annotations
 
@@ -40,6 +45,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="decode_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="time only the headline workload (by default the decode headline is followed by "
+                        "the tiny, prefill, skewed and fp8 workloads)")
+    p.add_argument("--side-steps", type=int, default=20, help="timed steps of each further workload")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="first run a plain device copy of this many MiB (the reference kernel for scaling "
@@ -140,14 +149,124 @@ def cpu_baseline(shape, tens, max_tokens, min_seconds=10.0, max_reps=8, dense=Fa
         if dense:
             oracle_ffn(tens, x=x, mats=mats)
         else:
-            oracle_forward(tens, x=x)
+            oracle_forward(tens, x=x, prefetch=False)
         dt += time.perf_counter() - t0
         reps += 1
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": n * reps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host_cores": len(os.sched_getaffinity(0)),
             "sample": f"first {n} of {shape.tokens} tokens of {shape.name}"
                       f"{'' if dense else ', all their experts'}, {reps} pass(es), "
-                      f"seconds={dt:.1f}"}
+                      f"seconds={dt:.1f}; numpy fp64 with {threads} BLAS threads on a host of "
+                      f"{len(os.sched_getaffinity(0))} usable cores"}
+
+
+def step_units(shape, counts):
+    """Algorithmic bytes and flops of one whole forward step (the method's own traffic: every
+    touched expert's weights once, the router weight and bias, x and the output) and the time the
+    MFMA peak needs for its flops (bf16 or fp32 router, expert GEMMs in the block's dtype)."""
+    D, E, K, I, S, T = shape.dim, shape.n_experts, shape.topk, shape.inter, shape.shared_inter, shape.tokens
+    wb = 1 if shape.dtype == "fp8" else (4 if shape.dtype == "f32" else 2)
+    xb = 4 if shape.dtype == "f32" else 2
+    touched = int((counts > 0).sum())
+    nbytes = (touched * 3 * I * D + 3 * S * D) * wb + E * D * xb + E * 4 + 2 * T * D * xb
+    if shape.dtype == "fp8":  # the fp32 128x128 block scales of the touched weights
+        nbytes += (touched * 3 * (I // 128) * (D // 128) + 3 * (S // 128) * (D // 128)) * 4
+    router_flops = 2 * T * D * E
+    expert_flops = 2 * 3 * D * (T * K * I + T * S)
+    peak_router = MFMA_PEAK_TFLOPS["f32" if shape.dtype == "f32" else "bf16"] * 1e12
+    t_mfma = router_flops / peak_router + expert_flops / (MFMA_PEAK_TFLOPS[shape.dtype] * 1e12)
+    return nbytes, router_flops + expert_flops, t_mfma
+
+
+def measure(shape, tens, blk, steps, warmup, dense):
+    """Warm up, time `steps` steps (HIP events around the dominant kernel's launches inside the
+    timed region), after an untimed pass of the same length with events around every launch that
+    gives the per-kernel breakdown and picks the dominant kernel."""
+    import torch
+
+    from mixture_experts_layer_14_amd import moe
+
+    out = torch.empty_like(tens.x)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        blk.forward(tens.x, out)
+    torch.cuda.synchronize()
+    T = shape.tokens
+    if dense:
+        counts, touched, units = None, None, ffn_units(shape)
+    else:
+        counts = blk.ws_view(T, "counts", torch.int32, shape.n_experts).cpu().numpy()
+        touched, units = kernel_units(shape, counts)
+
+    moe.timing_filter(None)
+    moe.timing_enable(True)
+    for _ in range(steps):
+        blk.forward(tens.x, out)
+    torch.cuda.synchronize()
+    kt = moe.timing_report()
+    moe.timing_enable(False)
+    kernels = {name: (cnt, tot / cnt) for name, (cnt, tot) in kt.items()}
+    dom = max(kernels, key=lambda n: kernels[n][0] * kernels[n][1])
+
+    moe.timing_filter(dom)
+    moe.timing_enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        blk.forward(tens.x, out)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    kt_dom = moe.timing_report()
+    moe.timing_enable(False)
+    moe.timing_filter(None)
+    dom_cnt, dom_tot = kt_dom[dom]
+    dom_ms = dom_tot / dom_cnt
+    kind = "gemm1" if ("gemm1" in dom or "<0" in dom) else ("gemm2" if ("gemm2" in dom or "<1" in dom) else None)
+    roof = None
+    if kind:
+        nbytes, flops = units[kind]
+        if T <= 256:
+            ach = nbytes / (dom_ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(dom, shape.name)}
+        else:
+            peak = MFMA_PEAK_TFLOPS[shape.dtype]
+            ach = flops / (dom_ms * 1e-3) / 1e12
+            roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(ach / peak, 4), "traffic": traffic_from_profiles(dom, shape.name)}
+        roof["kernel"] = dom
+        roof["avg_launch_ms"] = round(dom_ms, 5)
+    return dict(ms=ms, kernels=kernels, roof=roof, counts=counts, touched=touched)
+
+
+def block_config(shape, touched, seed):
+    return {"workload": shape.name, "tokens": shape.tokens, "dim": shape.dim, "experts": shape.n_experts,
+            "groups": shape.n_groups, "topk_groups": shape.topk_groups, "topk": shape.topk,
+            "inter": shape.inter, "shared": shape.n_shared, "touched_experts": touched, "seed": seed}
+
+
+def workload_summary(shape, m):
+    """One line of the `workloads` object: the whole step against its binding roof and against
+    the MFMA peak, plus the dominant kernel's roofline."""
+    nbytes, flops, t_mfma = step_units(shape, m["counts"])
+    sec = m["ms"] * 1e-3
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    return {
+        "ms_per_step": round(m["ms"], 4), "tokens_per_s": round(shape.tokens / sec, 1),
+        "dtype": shape.dtype, "touched_experts": m["touched"],
+        "step_bytes": nbytes, "step_flops": flops,
+        "hbm_frac": round(t_hbm / sec, 4), "mfma_frac": round(t_mfma / sec, 4),
+        "bound": bound, "bound_frac": round(max(t_hbm, t_mfma) / sec, 4),
+        "dominant": m["roof"],
+        "kernels_ms": {n: round(v[1], 5) for n, v in m["kernels"].items()},
+    }
+
+
+SIDE_WORKLOADS = ["tiny_fp32", "prefill_bf16", "skewed_bf16", "prefill_fp8"]
 
 
 def main():
@@ -156,7 +275,6 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
               f"multi-GPU path)", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
     from mixture_experts_layer_14_amd import inputs, moe
@@ -180,64 +298,11 @@ def main():
     else:
         tens = inputs.generate(shape, seed=args.seed, device=dev)
         blk = moe.Block(tens, shape.tokens)
-    out = torch.empty_like(tens.x)
-    stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        blk.forward(tens.x, out)
-    torch.cuda.synchronize()
+    print(f"[bench] {shape.name}: {args.steps} steps with per-kernel events, then {args.steps} timed",
+          file=sys.stderr, flush=True)
+    m = measure(shape, tens, blk, args.steps, args.warmup, dense)
+    ms, T = m["ms"], shape.tokens
 
-    T = shape.tokens
-    if dense:
-        touched, units = None, ffn_units(shape)
-    else:
-        counts = blk.ws_view(T, "counts", torch.int32, shape.n_experts).cpu().numpy()
-        touched, units = kernel_units(shape, counts)
-
-    # Per-kernel breakdown: K untimed steps with HIP events around every launch (they add a few
-    # microseconds per launch, so the timed steps below keep them on the dominant kernel only).
-    print(f"[bench] per-kernel pass, {args.steps} steps", file=sys.stderr, flush=True)
-    moe.timing_filter(None)
-    moe.timing_enable(True)
-    for _ in range(args.steps):
-        blk.forward(tens.x, out)
-    torch.cuda.synchronize()
-    kt = moe.timing_report()
-    moe.timing_enable(False)
-    kernels = {name: (cnt, tot / cnt) for name, (cnt, tot) in kt.items()}
-    dom = max(kernels, key=lambda n: kernels[n][0] * kernels[n][1])
-
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    moe.timing_filter(dom)
-    moe.timing_enable(True)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        blk.forward(tens.x, out)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    kt_dom = moe.timing_report()
-    moe.timing_enable(False)
-    moe.timing_filter(None)
-    dom_cnt, dom_tot = kt_dom[dom]
-    dom_ms = dom_tot / dom_cnt
-    kind = "gemm1" if ("gemm1" in dom or "<0" in dom) else ("gemm2" if ("gemm2" in dom or "<1" in dom) else None)
-    decode_like = T <= 256
-    roof = None
-    if kind:
-        nbytes, flops = units[kind]
-        if decode_like:
-            ach = nbytes / (dom_ms * 1e-3) / 1e9
-            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(dom, shape.name)}
-        else:
-            peak = MFMA_PEAK_TFLOPS[shape.dtype]
-            ach = flops / (dom_ms * 1e-3) / 1e12
-            roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(ach / peak, 4), "traffic": traffic_from_profiles(dom, shape.name)}
-        roof["kernel"] = dom
-        roof["avg_launch_ms"] = round(dom_ms, 5)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -246,9 +311,7 @@ def main():
     if dense:
         config = {"workload": shape.name, "tokens": T, "dim": shape.dim, "inter": shape.inter, "seed": args.seed}
     else:
-        config = {"workload": shape.name, "tokens": T, "dim": shape.dim, "experts": shape.n_experts,
-                  "groups": shape.n_groups, "topk_groups": shape.topk_groups, "topk": shape.topk,
-                  "inter": shape.inter, "shared": shape.n_shared, "touched_experts": touched, "seed": args.seed}
+        config = block_config(shape, m["touched"], args.seed)
     rec = {
         "metric": METRIC_DENSE if dense else METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1,
@@ -256,10 +319,32 @@ def main():
         "scaling": "weak", "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8": "fp8", "f32": "f32"}[shape.dtype], "data": "synthetic",
         "config": config,
-        "roofline": roof,
+        "roofline": m["roof"],
         "cpu_baseline": cpu,
-        "kernels_ms": {n: round(v[1], 5) for n, v in kernels.items()},
+        "kernels_ms": {n: round(v[1], 5) for n, v in m["kernels"].items()},
     }
+    if not dense:
+        rec["step"] = {k: v for k, v in workload_summary(shape, m).items() if k not in ("dominant", "kernels_ms")}
+
+    # The other workloads of the block, timed in the same run (not the headline value): the tiny
+    # fp32 block, the 4096-token bf16 prefill (HBM-bound), the skewed 4096-token prefill and the
+    # 16384-token fp8 prefill (MFMA-bound).
+    if not args.no_workloads and not dense and args.workload == "decode_bf16":
+        del blk, tens
+        torch.cuda.empty_cache()
+        rec["workloads"] = {}
+        for name in SIDE_WORKLOADS:
+            sh = inputs.WORKLOADS[name]
+            print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
+            tw = inputs.generate(sh, seed=args.seed, device=dev)
+            bw = moe.Block(tw, sh.tokens)
+            steps = max(args.side_steps, 1)
+            print(f"[bench] {name}: {steps} steps with per-kernel events, then {steps} timed",
+                  file=sys.stderr, flush=True)
+            mw = measure(sh, tw, bw, steps, max(args.warmup, 1), False)
+            rec["workloads"][name] = workload_summary(sh, mw)
+            del bw, tw
+            torch.cuda.empty_cache()
     print(json.dumps(rec), flush=True)
 
 

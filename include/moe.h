@@ -31,7 +31,9 @@
  *     launch and nothing is enqueued; launch failures return MOE_ERR_HIP.
  *     moe_last_error() then gives a message (thread-local, valid until the
  *     next call on that thread).
- *   - Non-finite inputs give unspecified results. T = 0 is a valid no-op.
+ *   - Non-finite inputs give unspecified values, never out-of-range indices:
+ *     a NaN selection score ranks below every number, so each token still gets
+ *     topk distinct experts in [0, n_experts). T = 0 is a valid no-op.
  *   - Two calls that share `ws` must be ordered on one stream.
  */
 #ifndef MOE_H
@@ -116,7 +118,9 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes);
  * Logits are fp32 values of exact dot products (bf16 or fp32 products summed in
  * fp64 per 32-element chunk); sigmoid, or softmax over the token's experts, is
  * evaluated in fp64 and rounded once; the sigmoid weights' sum runs in rank
- * order. n_groups = 1 is plain top-k over all experts. */
+ * order. n_groups = 1 is plain top-k over all experts. A token with a NaN score
+ * (NaN in its x, or a NaN bias) has that score ranked below every number; it
+ * still receives topk distinct experts, its weights are then unspecified. */
 moe_status moe_route(const moe_config* cfg, const void* w_gate, const float* bias, const void* x,
                      int64_t T, int32_t* idx, float* w, void* ws, size_t ws_bytes, void* stream);
 
@@ -128,7 +132,9 @@ moe_status moe_route(const moe_config* cfg, const void* w_gate, const float* bia
  *   row_token [T * K] out: rows grouped by expert ascending, tokens ascending
  *                     within an expert; row_token[r] = the token of row r
  *   row_of    [T, K]  out: the row of assignment (t, k)
- * idx values outside [0, E) give unspecified results. */
+ * An entry of idx outside [0, E) is not counted and gets row_of = -1 (the
+ * forward's combine skips such entries); a token listing one expert twice gives
+ * unspecified rows. */
 moe_status moe_dispatch(const moe_config* cfg, const int32_t* idx, int64_t T, int32_t* counts,
                         int32_t* offsets, int32_t* row_token, int32_t* row_of, void* ws,
                         size_t ws_bytes, void* stream);

@@ -53,9 +53,11 @@ __global__ __launch_bounds__(CT) void combine(const int32_t* __restrict__ idx, c
       // all rows are loaded before the in-order accumulation
       i32x4 rows[kMaxTopK];
 #pragma unroll
-      for (int k = 0; k < kMaxTopK; ++k)
-        if (k < K)
+      for (int k = 0; k < kMaxTopK; ++k) {
+        rows[k] = i32x4{0, 0, 0, 0};  // an assignment without a row (row_of < 0) adds zero
+        if (k < K && srow[k] >= 0)
           rows[k] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(O + (size_t)srow[k] * D + c));
+      }
       i32x4 v = ld16(SH + c);
 #pragma unroll
       for (int k = 0; k < kMaxTopK; ++k) {
@@ -84,7 +86,8 @@ __global__ __launch_bounds__(CT) void combine(const int32_t* __restrict__ idx, c
     float* Y = static_cast<float*>(out) + (size_t)t * D;
     for (int c = blockIdx.y * CT + threadIdx.x; c < D; c += gridDim.y * CT) {
       float y = 0.f;
-      for (int k = 0; k < K; ++k) y = y + O[(size_t)srow[k] * D + c] * sw[k];
+      for (int k = 0; k < K; ++k)
+        if (srow[k] >= 0) y = y + O[(size_t)srow[k] * D + c] * sw[k];
       Y[c] = y + SH[c];
     }
   }

@@ -183,7 +183,10 @@ __device__ void scatter_rows(const unsigned long long* bits, const int32_t* __re
   const unsigned long long below = (1ull << (threadIdx.x & 63)) - 1ull;
   for (int k = 0; k < K; ++k) {
     int e = idx[(size_t)t * K + k];
-    if ((unsigned)e >= (unsigned)E) continue;
+    if ((unsigned)e >= (unsigned)E) {  // no row: the combine skips this assignment
+      row_of[(size_t)t * K + k] = -1;
+      continue;
+    }
     int rank = __popcll(bits[e * WORDS + w] & below);
     for (int ww = 0; ww < w; ++ww) rank += __popcll(bits[e * WORDS + ww]);
     int row = base[e] + rank;

@@ -268,6 +268,9 @@ MOE_DEV double token_sum(double v, double* sh) {
   }
 }
 
+// -inf for NaN (a group of +inf and -inf scores sums to NaN): ranks below every group score
+MOE_DEV float nan_low(float v) { return __builtin_isnan(v) ? -INFINITY : v; }
+
 MOE_DEV void top2_merge(float& b, float& c, float b2, float c2) {
   const float hi = fmaxf(b, b2), lo = fminf(b, b2);
   c = fmaxf(lo, fmaxf(c, c2));
@@ -341,6 +344,9 @@ __global__ __launch_bounds__(256) void router_select(const double* __restrict__ 
     const float sv = softmax ? (float)(exp((double)zf[j] - (double)zmax) / zsum)
                              : (float)(1.0 / (1.0 + exp(-(double)zf[j])));
     sbv[j] = bias ? sv + bb[j] : sv;
+    // a NaN selection score (non-finite x or bias) ranks below every number, so the selection
+    // below still yields K distinct experts in [0, E), equal scores in ascending index order
+    if (__builtin_isnan(sbv[j])) sbv[j] = -INFINITY;
     if (e < E) {
       s_l[e] = sv;
       m_l[e] = sbv[j];
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(256) void router_select(const double* __restrict__ 
     if (lanes_path) {
       float b = sbv[j], c = -INFINITY;
       for (int off = gsize >> 1; off >= 1; off >>= 1) top2_merge(b, c, __shfl_xor(b, off), __shfl_xor(c, off));
-      if (e < E && e % gsize == 0) gsc[e / gsize] = bias ? b + c : b;
+      if (e < E && e % gsize == 0) gsc[e / gsize] = nan_low(bias ? b + c : b);
     }
   }
   __syncthreads();
@@ -359,7 +365,7 @@ __global__ __launch_bounds__(256) void router_select(const double* __restrict__ 
       float b = -INFINITY, c = -INFINITY;
       const float* v = m_l + tid * gsize;
       for (int i = 0; i < gsize; ++i) top2_merge(b, c, v[i], -INFINITY);
-      gsc[tid] = bias ? b + c : b;
+      gsc[tid] = nan_low(bias ? b + c : b);
     }
     __syncthreads();
   }

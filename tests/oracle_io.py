@@ -15,8 +15,37 @@ def codes(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").contiguous().view(torch.uint8).numpy()
 
 
-def expert_fn(tens, device_to_host=True):
-    """(expert(e), shared()) accessors returning fp64 [out, in] matrices for the oracle."""
+class _Prefetch:
+    """expert(e) with the next few experts' fp64 matrices prepared on worker threads (the oracle
+    asks for experts in ascending order; the copies and fp8 dequantisations release the GIL).
+    Plumbing only: every value comes from `load(e)` unchanged."""
+
+    def __init__(self, load, n_experts, depth=4):
+        from concurrent.futures import ThreadPoolExecutor
+
+        self.load, self.n, self.depth = load, n_experts, depth
+        self.pool = ThreadPoolExecutor(max_workers=depth)
+        self.pending = {}
+        self.last_report = -1
+
+    def __call__(self, e):
+        for j in range(e, min(self.n, e + self.depth + 1)):
+            if j not in self.pending:
+                self.pending[j] = self.pool.submit(self.load, j)
+        for j in [j for j in self.pending if j < e]:
+            self.pending.pop(j).cancel()
+        if e // 32 != self.last_report:  # progress of a long oracle run
+            self.last_report = e // 32
+            print(f"    oracle: expert {e} of {self.n}", flush=True)
+        return self.pending.pop(e).result()
+
+    def __del__(self):
+        self.pool.shutdown(wait=False, cancel_futures=True)
+
+
+def expert_fn(tens, prefetch=False):
+    """(expert(e), shared()) accessors returning fp64 [out, in] matrices for the oracle; with
+    prefetch, the following experts are prepared on worker threads while one is in use."""
     fp8 = tens.shape.dtype == "fp8"
 
     def mat(w, s):
@@ -34,6 +63,8 @@ def expert_fn(tens, device_to_host=True):
             return mat(tens.ws1, tens.ss1), mat(tens.ws3, tens.ss3), mat(tens.ws2, tens.ss2)
         return exact(tens.ws1), exact(tens.ws3), exact(tens.ws2)
 
+    if prefetch:
+        return _Prefetch(expert, tens.shape.n_experts), shared
     return expert, shared
 
 
@@ -46,9 +77,12 @@ def bias_np(tens):
     return None if tens.bias is None else tens.bias.detach().cpu().numpy().astype(np.float32)
 
 
-def oracle_forward(tens, x=None):
-    """Run the oracle block on tens (optionally on a subset of tokens x [n, D] fp64)."""
-    expert, shared = expert_fn(tens)
+def oracle_forward(tens, x=None, prefetch=None):
+    """Run the oracle block on tens (optionally on a subset of tokens x [n, D] fp64). Experts are
+    prefetched on worker threads for full-size weights (dim >= 4096) unless told otherwise."""
+    if prefetch is None:
+        prefetch = tens.shape.dim >= 4096
+    expert, shared = expert_fn(tens, prefetch=prefetch)
     act, out = act_out(tens.shape)
     xx = exact(tens.x) if x is None else x
     return O.moe_forward(tens.shape, xx, exact(tens.w_gate), bias_np(tens), expert, shared, act, out)

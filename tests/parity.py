@@ -4,8 +4,11 @@ Routing: expert indices must equal the oracle's, order included; a token may dif
 oracle flags it as a near-tie (a score gap below 1e-6 at the kept-group boundary, the K-th expert
 boundary, or between two chosen experts), and at most 0.01% of the tokens may differ.
 Weights: within 4 ulp of the oracle's where the indices agree.
+A token that differs must still be a valid group-limited top-k of the oracle's fp32 scores when
+every gap below 1e-6 may be resolved either way.
 Dispatch: counts, offsets, row_token and row_of equal the oracle's dispatch of the GPU's indices.
-Outputs: relative L2 error (fp64) at most 1e-4 (fp32 blocks), 1e-2 (bf16), 5e-2 (fp8).
+Outputs: relative L2 error (fp64) at most 1e-4 (fp32 blocks), 1e-2 (bf16), 5e-2 (fp8), both over
+all compared values and for every compared token on its own.
 """
 import math
 import sys
@@ -28,6 +31,40 @@ def np_i32(t):
     return t.detach().to("cpu").numpy().astype(np.int64)
 
 
+def valid_selection(shape, r, t, sel, thresh=NEAR_TIE):
+    """Is `sel` (the K experts a kernel chose for token t, in its order) a valid group-limited
+    top-k of the oracle's fp32 scores of token t, if every gap below `thresh` may go either way?
+    The kept groups must be the touched ones plus the best others; each touched group within
+    thresh of the Gk-th group score; each chosen expert within thresh of the K-th best score of
+    the kept groups; the order descending within thresh."""
+    E, G, Gk, K = shape.n_experts, shape.n_groups, shape.topk_groups, shape.topk
+    sel = np.asarray(sel, dtype=np.int64)
+    if len(set(sel.tolist())) != K or sel.min() < 0 or sel.max() >= E:
+        return False
+    sb = r.sb[t].astype(np.float64)
+    gsize = E // G
+    kept = np.ones(G, dtype=bool)
+    if G > 1 and r.group_scores is not None and Gk < G:
+        gs = r.group_scores[t].astype(np.float64)
+        touched = np.unique(sel // gsize)
+        if len(touched) > Gk:
+            return False
+        gk_th = np.sort(gs)[::-1][Gk - 1]
+        if (gs[touched] < gk_th - thresh).any():
+            return False
+        kept = np.zeros(G, dtype=bool)
+        kept[touched] = True
+        for g in np.argsort(-gs, kind="stable"):
+            if kept.sum() >= Gk:
+                break
+            kept[g] = True
+    cand = np.where(np.repeat(kept, gsize), sb, -np.inf)
+    kth = np.sort(cand)[::-1][K - 1]
+    if (cand[sel] < kth - thresh).any():
+        return False
+    return bool((np.diff(sb[sel]) <= thresh).all())
+
+
 def route_check(shape, oracle_route, gpu_idx, gpu_w):
     """Returns (mismatched token mask, report dict); asserts the routing rules."""
     oi = oracle_route.idx.astype(np.int64)
@@ -41,6 +78,8 @@ def route_check(shape, oracle_route, gpu_idx, gpu_w):
                flagged_order=int(flags.order.sum()))
     assert not (bad & ~flags.any).any(), f"unflagged routing mismatch: {rep}"
     assert bad.sum() <= math.floor(1e-4 * n), f"too many near-tie mismatches: {rep}"
+    for t in np.nonzero(bad)[0]:
+        assert valid_selection(shape, oracle_route, t, gi[t]), f"token {t}: {gi[t]} is no valid top-k: {rep}"
     ow = oracle_route.w
     gw = np.asarray(gpu_w, dtype=np.float32)
     ok = ~bad
@@ -81,11 +120,38 @@ def out_check(shape, gpu_out, oracle_out, skip=None):
     if skip is not None and skip.any():
         g, o = g[~skip], o[~skip]
     err = rel_l2(g, o)
-    per_tok = [rel_l2(g[i], o[i]) for i in range(g.shape[0])]
-    rep = dict(rel_l2=err, max_token_rel_l2=max(per_tok) if per_tok else 0.0, tol=REL_L2[shape.dtype])
+    per_tok = np.array([rel_l2(g[i], o[i]) for i in range(g.shape[0])])
+    tol = REL_L2[shape.dtype]
+    worst = int(per_tok.argmax()) if per_tok.size else -1
+    rep = dict(rel_l2=err, max_token_rel_l2=float(per_tok.max()) if per_tok.size else 0.0, tol=tol,
+               tokens=int(g.shape[0]))
     assert np.isfinite(g).all()
-    assert err <= REL_L2[shape.dtype], rep
+    assert err <= tol, rep
+    assert (per_tok <= tol).all(), dict(rep, worst_token=worst, over=int((per_tok > tol).sum()))
     return rep
+
+
+def tile_tokens(T, counts, offsets, row_token, bm, rng, per_expert="all", shared_stride=1):
+    """Tokens such that the compared outputs hold at least one row of every `bm`-row M-tile the
+    GEMM kernels ran: per routed expert every M-tile (per_expert="all") or its first, a middle
+    and its last one ("ends"), each M-tile's row drawn at random except the last (ragged) tile's,
+    which is its last row; then every `shared_stride`-th M-tile of the shared expert (tokens
+    j*bm .. j*bm+bm-1) and the last token."""
+    counts = np.asarray(counts)
+    offsets = np.asarray(offsets)
+    row_token = np.asarray(row_token)
+    toks = [T - 1]
+    for e in np.nonzero(counts)[0]:
+        c = int(counts[e])
+        mt = (c + bm - 1) // bm
+        tiles = range(mt) if per_expert == "all" else sorted({0, mt // 2, mt - 1})
+        for m in tiles:
+            last = min(c, (m + 1) * bm) - 1
+            row = last if m == mt - 1 else m * bm + int(rng.integers(0, bm))
+            toks.append(int(row_token[offsets[e] + row]))
+    for j in range(0, (T + bm - 1) // bm, shared_stride):
+        toks.append(min(T - 1, j * bm + int(rng.integers(0, bm))))
+    return np.unique(np.asarray(toks, dtype=np.int64))
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:

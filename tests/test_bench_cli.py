@@ -47,3 +47,19 @@ def test_committed_traffic_entries_are_well_formed():
         assert rec["bytes_per_launch"] > 0
         assert abs(rec["fetch_scale"] - 2.0) < 0.01 and abs(rec["write_scale"] - 1.0) < 0.01
         assert len(rec["source_hash"]) == 16
+
+
+def test_step_units_match_the_page_figures():
+    """Whole-step flops are 796,393,472 per token (every used parameter but the bias, twice); the
+    bytes of a step that touches every expert are the block's weights plus x and the output."""
+    import numpy as np
+
+    sh = inputs.WORKLOADS["prefill_bf16"]
+    nbytes, flops, t_mfma = bench.step_units(sh, np.ones(256, dtype=np.int64))
+    assert flops == 4096 * 796_393_472
+    assert nbytes == 22_640_329_728 + 2 * 4096 * 7168 * 2
+    assert abs(t_mfma - flops / 2.5e15) < 1e-12
+    fp8 = inputs.WORKLOADS["prefill_fp8"]
+    nb8, fl8, t8 = bench.step_units(fp8, np.ones(256, dtype=np.int64))
+    router = 2 * 16384 * 7168 * 256
+    assert fl8 == 16384 * 796_393_472 and abs(t8 - (router / 2.5e15 + (fl8 - router) / 5e15)) < 1e-12

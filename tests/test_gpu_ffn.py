@@ -4,14 +4,16 @@ Small shapes are checked on every token at token counts that take each kernel pa
 stream / fp8 kernels below 64 tokens, the weight-stream, ring and 128-row kernels above) with
 ragged tails whose last 128-row tile has 1, 2, 3 or 4 live 32-row groups (129, 64 / 300, 96 / 200,
 128 tokens); the DeepSeek-V3 dense layer (dim 7168, intermediate 18,432) is checked at the
-decode, prefill and FP8-prefill token counts on every token (decode) or sampled tokens."""
+decode, prefill and FP8-prefill token counts on every token (16 and 4096 tokens) or on a token of
+every 128-row M-tile (16384 fp8 tokens, and past the kernels' 2 GB range a token of every M-tile
+of the kernels that run there). Every compared token is held to the tolerance on its own."""
 import numpy as np
 import pytest
 import torch
 
 from mixture_experts_layer_14_amd import inputs, moe
 from tests.oracle_io import exact, ffn_mats, oracle_ffn
-from tests.parity import out_check, say, to_np
+from tests.parity import out_check, say, tile_tokens, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -66,8 +68,9 @@ def test_ffn_full_shape(name):
     say(f"[ffn/full] {name} T={T} D={shape.dim} I={shape.inter} dtype={shape.dtype}: generating weights")
     tens = inputs.generate_ffn(shape, seed=0, device=DEV)
     _, out = run_ffn(tens, T)
+    # every token up to 4096; at 16384 (fp8) a token of every 128-row M-tile
     rng = np.random.default_rng(1)
-    sample = np.arange(T) if T <= 16 else np.unique(np.concatenate([[0, T - 1], rng.choice(T, 10, replace=False)]))
+    sample = np.arange(T) if T <= 4096 else tile_tokens(T, [], [0], [], 128, rng)
     say(f"  oracle on {len(sample)} tokens")
     want = oracle_ffn(tens, x=exact(tens.x)[sample], mats=ffn_mats(tens))
     rep = out_check(shape, to_np(out)[sample], want)
@@ -94,8 +97,9 @@ def test_ffn_beyond_2gb_activations(name, T):
     say(f"[ffn/beyond 2 GB] {name} T={T}: generating weights")
     tens = inputs.generate_ffn(shape, seed=4, device=DEV)
     _, out = run_ffn(tens, T)
+    # a token of every M-tile the kernels ran (256 rows in bf16, 128 in fp8)
     rng = np.random.default_rng(4)
-    sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 8, replace=False)]))
+    sample = tile_tokens(T, [], [0], [], 256 if shape.dtype == "bf16" else 128, rng)
     want = oracle_ffn(tens, x=exact(tens.x[torch.as_tensor(sample, device=tens.x.device)]), mats=ffn_mats(tens))
     got = to_np(out[torch.as_tensor(sample, device=out.device)])
     say(f"  out {out_check(shape, got, want)}")

@@ -1,9 +1,11 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded synthetic inputs.
 
-Small shapes are checked on every token and span several tiles with ragged tails; the full
-DeepSeek-V3 shapes (decode 16, prefill 4096, skewed 4096, fp8 16384 tokens) are checked on
-routing and dispatch for every token and on the outputs of sampled tokens, in the launch
-configuration the bench times."""
+Small shapes are checked on every token and span several tiles with ragged tails. The full
+DeepSeek-V3 shapes are checked in the launch configuration the bench times: routing and dispatch
+on every token; outputs on every token at 16 and 4096 tokens (decode, prefill, skewed), and at
+16384 fp8 tokens on a sample holding a row of every 128-row M-tile of every expert (each expert's
+ragged last tile by its last row) and of the shared expert. Every compared token is held to the
+tolerance on its own as well as in aggregate."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +13,7 @@ import torch
 from mixture_experts_layer_14_amd import inputs, moe
 from oracle import moe_oracle as O
 from tests.oracle_io import bias_np, exact, oracle_forward
-from tests.parity import dispatch_check, np_i32, out_check, route_check, say, to_np
+from tests.parity import dispatch_check, np_i32, out_check, route_check, say, tile_tokens, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -114,10 +116,12 @@ def test_forward_full_shape(name):
     gidx, gw = gpu_route(blk, shape, T)
     bad, rep = route_check(shape, r, gidx, gw)
     say(f"  route {rep}")
-    dispatch_check(shape, gidx, *gpu_dispatch(blk, shape, T))
-    rng = np.random.default_rng(1)
-    n = T if T <= 16 else 10
-    sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n, replace=False)]))[:max(n, 2)]
+    counts, offsets, row_token, _ = gpu_dispatch(blk, shape, T)
+    dispatch_check(shape, gidx, counts, offsets, row_token, gpu_dispatch(blk, shape, T)[3])
+    if T <= 4096:
+        sample = np.arange(T)
+    else:  # a row of every 128-row M-tile the fp8 GEMMs ran
+        sample = tile_tokens(T, counts, offsets, row_token, 128, np.random.default_rng(1))
     say(f"  oracle forward on {len(sample)} tokens")
     f = oracle_forward(tens, x=exact(tens.x)[sample])
     orep = out_check(shape, to_np(out)[sample], f.out, skip=bad[sample])
@@ -182,9 +186,17 @@ def test_forward_beyond_2gb_activations(name, T):
     gidx, gw = gpu_route(blk, shape, T)
     bad, rep = route_check(shape, r, gidx, gw)
     say(f"  route {rep}")
-    dispatch_check(shape, gidx, *gpu_dispatch(blk, shape, T))
+    counts, offsets, row_token, row_of = gpu_dispatch(blk, shape, T)
+    dispatch_check(shape, gidx, counts, offsets, row_token, row_of)
+    # each expert's first, middle and last (ragged) M-tile of the kernels that run here (256-row
+    # ring tiles in bf16, 128-row tiles in fp8), every fourth shared-expert M-tile, and tokens
+    # whose x row starts past the 2 GB byte offset
     rng = np.random.default_rng(4)
-    sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 8, replace=False)]))
+    bm = 256 if shape.dtype == "bf16" else 128
+    past = (2 ** 31) // (shape.dim * (2 if shape.dtype == "bf16" else 1)) + 1
+    sample = np.unique(np.concatenate([
+        tile_tokens(T, counts, offsets, row_token, bm, rng, per_expert="ends", shared_stride=4),
+        rng.integers(past, T, 16)]))
     say(f"  oracle forward on {len(sample)} tokens")
     f = oracle_forward(tens, x=xe[sample])
     got = to_np(out[torch.as_tensor(sample, device=out.device)])
@@ -388,3 +400,104 @@ def test_two_streams_two_workspaces():
             bb.forward(tb.x, ob)
         torch.cuda.synchronize()
         assert torch.equal(oa, ref_a) and torch.equal(ob, ref_b)
+
+
+def _oracle_h_fp8(tens, rows_tok, rows_exp, e_shared):
+    """The oracle's e4m3 codes and 1x128 scales of h for the given (token, expert) rows: h from the
+    x image the GEMMs read, W1 and W3 dequantised, rounded to fp32, then requantised (R7, R9)."""
+    from tests.oracle_io import expert_fn
+
+    expert, shared = expert_fn(tens)
+    xa = O.activation_input(exact(tens.x), "fp8")
+    codes = np.empty((len(rows_tok), tens.shape.inter), np.uint8)
+    scales = np.empty((len(rows_tok), tens.shape.inter // 128), np.float32)
+    for e in np.unique(rows_exp):
+        sel = np.nonzero(rows_exp == e)[0]
+        w1, w3, _ = shared() if e == e_shared else expert(int(e))
+        x = xa[rows_tok[sel]]
+        g, u = x @ w1.T, x @ w3.T
+        h = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
+        codes[sel], scales[sel] = O.quant_1x128(h)
+    return codes, scales
+
+
+@pytest.mark.parametrize("name,T", [("wstream_fp8", 600), ("big_expert_fp8", 3000), ("mid_fp8", 200),
+                                    ("mid_fp8", 40)])
+def test_fp8_h_codes_match_oracle(name, T):
+    """The gate/up kernels' fused SwiGLU + requantisation epilogue (weight-stream kernels at 600 and
+    3000 tokens, 128-row kernels at 200, 16-row kernels at 40), on every routed and shared row.
+
+    The kernels form h from fp32 sums of exact fp8 products promoted per 128-k block, the oracle
+    from an fp64 sum: h differs by up to ~1e-4 of its block's amax. So each 1x128 scale (amax / 448)
+    is within 1e-3 relative of the oracle's, and each code's value in scaled units (code value =
+    h / scale) is within one e4m3 step of the larger of the two, plus 448 x 1e-4 for the h error
+    (which near zero spans several subnormal steps); at least 99% of the codes are equal. A wrong
+    scale rule or block shape moves scales by O(1); truncation instead of round-to-nearest-even
+    changes about half of the codes."""
+    shape = SMALL[name].with_tokens(T)
+    K, I = shape.topk, shape.inter
+    say(f"[fp8 h codes] {name} T={T}")
+    tens = inputs.generate(shape, seed=14, device=DEV)
+    blk, _ = run_block(tens)
+    R = T * K
+    counts, offsets, row_token, _ = gpu_dispatch(blk, shape, T)
+    row_exp = np.repeat(np.arange(shape.n_experts), counts)
+    hq = np.concatenate([blk.ws_view(T, "h_routed", torch.uint8, R * I).view(R, I).cpu().numpy(),
+                         blk.ws_view(T, "h_shared", torch.uint8, T * I).view(T, I).cpu().numpy()])
+    hs = np.concatenate([blk.ws_view(T, "h_scale", torch.float32, R * I // 128).view(R, I // 128).cpu().numpy(),
+                         blk.ws_view(T, "h_shared_scale", torch.float32, T * I // 128).view(T, I // 128).cpu().numpy()])
+    toks = np.concatenate([row_token, np.arange(T)])
+    exps = np.concatenate([row_exp, np.full(T, shape.n_experts)])
+    oq, osc = _oracle_h_fp8(tens, toks, exps, shape.n_experts)
+    rel = np.abs(hs.astype(np.float64) - osc) / osc
+    qg, qo = O.e4m3_decode(hq), O.e4m3_decode(oq)
+    mag = np.maximum(np.abs(qg), np.abs(qo))
+    # one e4m3 step at that magnitude: 2^(e - 3) for normals (e >= -6), 2^-9 below
+    ulp = 2.0 ** (np.maximum(np.floor(np.log2(np.maximum(mag, 2.0 ** -9))), -6) - 3)
+    excess = np.abs(qg - qo) / (ulp + 448 * 1e-4)
+    rep = dict(rows=len(toks), scale_max_rel=float(rel.max()), codes_equal=float((qg == qo).mean()),
+               worst_code_diff_over_bound=float(excess.max()))
+    say(f"  {rep}")
+    assert rel.max() <= 1e-3, rep
+    assert excess.max() <= 1.0 and (qg == qo).mean() >= 0.99, rep
+
+
+@pytest.mark.parametrize("name,T", [("mid_bf16", 40), ("mid_bf16", 300), ("mid_fp8", 200)])
+def test_nan_token_still_routes_to_valid_experts(name, T):
+    """A token whose x holds a NaN has NaN logits; its selection scores rank below every number, so
+    it still gets K distinct experts in [0, E) (the lowest indices of the lowest kept groups) and
+    nothing downstream reads outside its buffers. Every other token routes and computes exactly as
+    without it (a block per token at 40 tokens, a wave per token at 300)."""
+    shape = SMALL[name].with_tokens(T)
+    say(f"[nan token] {name} T={T}")
+    tens = inputs.generate(shape, seed=15, device=DEV)
+    nan_tok = T // 3
+    tens.x[nan_tok, 5] = float("nan")
+    blk, out = run_block(tens)
+    gidx, gw = gpu_route(blk, shape, T)
+    assert ((gidx >= 0) & (gidx < shape.n_experts)).all()
+    assert all(len(set(r.tolist())) == shape.topk for r in gidx)
+    others = np.setdiff1d(np.arange(T), [nan_tok])
+    f = oracle_forward(tens, x=exact(tens.x)[others])
+    bad, rep = route_check(shape, f.route, gidx[others], gw[others])
+    counts, offsets, row_token, row_of = gpu_dispatch(blk, shape, T)
+    dispatch_check(shape, gidx, counts, offsets, row_token, row_of)
+    got = to_np(out)
+    say(f"  route {rep}\n  out {out_check(shape, got[others], f.out, skip=bad)}")
+
+
+def test_nan_bias_expert_is_never_chosen():
+    """A NaN selection bias ranks that expert below every number: routing equals the oracle's with
+    that bias at -inf (the expert is never chosen while enough others remain)."""
+    shape = SMALL["mid_bf16"]
+    tens = inputs.generate(shape, seed=16, device=DEV)
+    tens.bias[9] = float("nan")
+    blk, out = run_block(tens)
+    T = shape.tokens
+    gidx, gw = gpu_route(blk, shape, T)
+    b = bias_np(tens)
+    b[9] = -np.inf
+    r = O.route(shape, exact(tens.x), exact(tens.w_gate), b)
+    route_check(shape, r, gidx, gw)
+    assert not (gidx == 9).any()
+    assert np.isfinite(to_np(out)).all()
