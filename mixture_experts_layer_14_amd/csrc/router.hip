@@ -461,7 +461,7 @@ __global__ __launch_bounds__(256) void router_select(const double* __restrict__ 
 static bool router_wide(const Dims& d) { return d.dtype != 0 && d.T >= 1024; }
 
 int router_splits(const Dims& d) {
-  if (d.dtype == 0) return 1;
+  if (d.dtype == 0 || d.T == 0) return 1;
   const bool wide = router_wide(d);
   int64_t tiles = wide ? ((d.T + 63) / 64) * ((d.E + 255) / 256) : ((d.T + 31) / 32) * ((d.E + 31) / 32);
   // enough blocks to stream the router weight with many CUs, but few slices to add up, each

@@ -154,3 +154,14 @@ def test_ffn_host_checks_without_gpu():
     assert L.moe_ffn(ctypes.byref(cfg), ctypes.byref(w), 0x1000, -1, 0x2000, 0x3000, 1 << 40, None) == -1
     cfg8 = moe.ffn_config(inputs.FFN_WORKLOADS["dense_prefill_fp8"])
     assert L.moe_ffn(ctypes.byref(cfg8), ctypes.byref(w), 0x1000, 16, 0x2000, 0x3000, 1 << 40, None) == -1
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_workspace_size_of_zero_tokens(dtype):
+    """T = 0 is valid everywhere: its workspace size is a small positive number (no division by the
+    empty token count when the router's k-split is planned)."""
+    st, n = status_of_size(cfg_of(dtype=dtype), 0)
+    assert st == 0 and 0 < n < 1 << 20
+    f = moe.FfnConfig(7168, 18432, {"f32": 0, "bf16": 1, "fp8": 2}[dtype])
+    size = ctypes.c_size_t()
+    assert moe.lib().moe_ffn_workspace_size(ctypes.byref(f), 0, ctypes.byref(size)) == 0
