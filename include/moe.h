@@ -145,6 +145,23 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* idx, int64_t T, in
 moe_status moe_forward(const moe_config* cfg, const moe_weights* wts, const void* x, int64_t T,
                        void* out, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, results and errors as moe_forward,
+ * except that the workspace is the library's own static device array of
+ * MOE_STATIC_SCRATCH_BYTES (64 MiB; enough for about 380 tokens of the full
+ * DeepSeek-V3 bf16 block), held on each device the library runs on until the
+ * process ends. Nothing is allocated or freed by this call. Errors, besides
+ * those of moe_forward: MOE_ERR_UNSUPPORTED when T needs a larger workspace
+ * than that (checked on the host before any launch), MOE_ERR_HIP when the
+ * array's device address cannot be found. Every call on one device uses the
+ * same array: calls that overlap on one device (two streams, two host threads)
+ * race and give undefined results; calls ordered on one stream are safe. The
+ * array keeps the last call's intermediates; no call needs it cleared. */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_static(const moe_config* cfg, const moe_weights* wts, const void* x, int64_t T,
+                              void* out, void* stream);
+
 /* Byte offsets inside the forward workspace of intermediates that tests read
  * after moe_forward has run (in stream order). Sizes: idx, w [T*K]; counts [E];
  * offsets [E+1]; row_token, row_of [T*K]; h_routed [T*K, I] and h_shared [T, S]

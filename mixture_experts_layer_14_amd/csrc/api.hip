@@ -11,6 +11,9 @@
 #include "../../include/moe.h"
 #include "kernels.h"
 
+// The workspace of moe_forward_static: one copy per device, held until the process ends.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -176,6 +179,30 @@ moe_status check_ws(const Layout& L, const void* ws, size_t ws_bytes) {
                                        std::to_string(L.pub.total));
   if (!ws && L.pub.total) return fail(MOE_ERR_ARG, "ws is NULL");
   if (!aligned16(ws)) return fail(MOE_ERR_ARG, "ws is not 16-byte aligned");
+  return MOE_OK;
+}
+
+// ---- the allocation-free forward (moe_forward_static): one workspace per device in the
+// file-scope device array `scratch` (declared above the anonymous namespace). In host code
+// `scratch` names a host-side stand-in; the device address comes from hipGetSymbolAddress, once
+// per device with that device current, and only that address is used.
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_at;  // device -> address of that device's copy of `scratch`
+
+moe_status static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_at.find(dev);
+  if (it == g_scratch_at.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    it = g_scratch_at.emplace(dev, p).first;
+  }
+  *ptr = it->second;
   return MOE_OK;
 }
 
@@ -453,6 +480,23 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wts, const void
   act.o_shared = at<void>(ws, L.pub.o_shared);
   if ((st = hip_status(moe::launch_experts(d, ep, act, s), "experts")) != MOE_OK) return st;
   return hip_status(moe::launch_combine(d, idx, w, row_of, act.o_routed, act.o_shared, out, s), "combine");
+}
+
+moe_status moe_forward_static(const moe_config* cfg, const moe_weights* wts, const void* x, int64_t T, void* out,
+                              void* stream) {
+  moe::Dims d;
+  moe_status st = check_config(cfg, T, &d);
+  if (st != MOE_OK) return st;
+  const size_t need = plan(d).pub.total;
+  if (need > (size_t)MOE_STATIC_SCRATCH_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED, "T = " + std::to_string(T) + " needs " + std::to_string(need) +
+                                         " bytes of workspace; the static scratch holds " +
+                                         std::to_string((size_t)MOE_STATIC_SCRATCH_BYTES) +
+                                         " (use moe_forward with a caller workspace)");
+  if (T == 0) return wts ? MOE_OK : fail(MOE_ERR_ARG, "wts is NULL");
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws)) != MOE_OK) return st;
+  return moe_forward(cfg, wts, x, T, out, ws, (size_t)MOE_STATIC_SCRATCH_BYTES, stream);
 }
 
 moe_status moe_ffn_workspace_size(const moe_ffn_config* cfg, int64_t T, size_t* bytes) {

@@ -156,6 +156,29 @@ def test_ffn_host_checks_without_gpu():
     assert L.moe_ffn(ctypes.byref(cfg8), ctypes.byref(w), 0x1000, 16, 0x2000, 0x3000, 1 << 40, None) == -1
 
 
+def test_static_forward_rejects_tokens_beyond_its_scratch_on_the_host():
+    """moe_forward_static refuses, before any device call, a token count whose workspace exceeds
+    the library's static array, naming both sizes; T = 0 is a no-op; argument errors come first."""
+    L = moe.lib()
+    cfg = cfg_of()
+    wts = moe.MoeWeights()
+    too_many = 1
+    while status_of_size(cfg, too_many)[1] <= moe.STATIC_SCRATCH_BYTES:
+        too_many *= 2
+    st = L.moe_forward_static(ctypes.byref(cfg), ctypes.byref(wts), None, too_many, None, None)
+    assert st == -5
+    msg = L.moe_last_error().decode()
+    assert "static scratch" in msg and str(moe.STATIC_SCRATCH_BYTES) in msg
+    assert L.moe_forward_static(ctypes.byref(cfg), ctypes.byref(wts), None, 0, None, None) == 0
+    assert L.moe_forward_static(ctypes.byref(cfg), None, None, 0, None, None) == -1
+    assert L.moe_forward_static(None, ctypes.byref(wts), None, 4, None, None) == -1
+    bad = cfg_of(topk=40)
+    assert L.moe_forward_static(ctypes.byref(bad), ctypes.byref(wts), None, 4, None, None) in (-2, -5)
+    # the limit in the binding is the header's
+    text = open(HEADER).read()
+    assert "#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)" in text and moe.STATIC_SCRATCH_BYTES == 64 << 20
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
 def test_workspace_size_of_zero_tokens(dtype):
     """T = 0 is valid everywhere: its workspace size is a small positive number (no division by the
