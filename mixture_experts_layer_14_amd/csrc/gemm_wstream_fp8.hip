@@ -16,7 +16,10 @@
 //
 // A step's partial products come from two 32x32x64 fp8 MFMAs started from zero per 32 x 32 tile;
 // they are added to the fp32 accumulators times sx(row) * sw, sw being the weight scale of the
-// step's block (a scalar load). The MFMAs take the weights as their first operand, so the 16
+// step's block. Both scales reach LDS with the stage (the row scales through waves 0-3's 4-byte
+// loads, the step's weight scales through waves 4 and 5's), so the loop has no scalar memory
+// loads: a scalar load shares the LDS wait counter, and waiting for it stalled every step on the
+// scalar cache and drained the fragment reads in flight. The MFMAs take the weights as their first operand, so the 16
 // elements of a lane belong to one activation row and share sx: a promotion costs one product per
 // scale and one FMA per element, and the other wave of the SIMD issues MFMAs meanwhile.
 //
@@ -37,7 +40,7 @@ constexpr int WQ_WAVES = 8;
 constexpr int WQ_BM = kWideBM;                                   // rows per M-tile (128)
 constexpr int WQ_NS = 3;                                         // stages and slabs per wave
 constexpr int WQ_A = WQ_BM * 128;                                // 16 KB per activation stage
-constexpr int WQ_SX = WQ_WAVES * 256;                            // row scales: wave w's 64 lanes x 4 B
+constexpr int WQ_SX = WQ_WAVES * 256;                            // scales: wave w's 64 lanes x 4 B
 constexpr int WQ_SLAB = 32 * 128;                                // 4 KB per weight slab
 constexpr int WQ_AQ = WQ_BM / 8 / WQ_WAVES;                      // activation loads per wave and step (2)
 constexpr int WQ_BQ = 4;                                         // weight loads per wave and step
@@ -173,7 +176,6 @@ __global__ __launch_bounds__(64 * WQ_WAVES) void gemm_wstream_fp8(
   auto a_set = [&](const WsItem& d, int tok_mine) __attribute__((always_inline)) {
     const int ln = lane_now();
     a_base = MODE == 0 ? aq : (d.sh ? h_shared_in : h_routed_in);
-    s_base = MODE == 0 ? a_scale : (d.sh ? hs_shared_in : hs_routed_in);
     a_rot = d.rot;
     const int row_bytes = MODE == 0 ? D : (d.sh ? S : I);
 #pragma unroll
@@ -191,7 +193,20 @@ __global__ __launch_bounds__(64 * WQ_WAVES) void gemm_wstream_fp8(
     }
     const int s_row = wave * 32 + ln;
     const int tok_s = MODE == 0 ? tok_mine : d.row0 + s_row;
-    s_voff = (d.live && wave < 4 && ln < 32 && s_row < d.nrows) ? tok_s * (nk * 4) : WS_OOB;
+    if (wave < 4) {  // the tile rows' scales
+      s_base = MODE == 0 ? a_scale : (d.sh ? hs_shared_in : hs_routed_in);
+      s_voff = (d.live && ln < 32 && s_row < d.nrows) ? tok_s * (nk * 4) : WS_OOB;
+    } else {  // the weight scale of the step's block: waves 4 and 5, lane 0
+      if (MODE == 0) {  // wave 4: W1's 128x128 block row holding the item's h-columns, wave 5: W3's
+        const size_t nb = I / 128;
+        s_base = (wave == 4 ? (d.sh ? ssa : sa + (size_t)d.expert * nb * nk)
+                            : (d.sh ? ssb : sb_ + (size_t)d.expert * nb * nk)) + (size_t)d.nt * nk;
+      } else {  // wave 4: the W2 block row of waves 0-3's output columns, wave 5: that of waves 4-7
+        const size_t nb = D / 128;
+        s_base = (d.sh ? ssa : sa + (size_t)d.expert * nb * nk) + (size_t)(d.nt * 2 + (wave & 1)) * nk;
+      }
+      s_voff = (d.live && wave < 6 && ln == 0) ? 0 : WS_OOB;
+    }
   };
   auto issue_a = [&](int stage, int ks) __attribute__((always_inline)) {
     const int kbi = blk(ks, a_rot);
@@ -200,7 +215,7 @@ __global__ __launch_bounds__(64 * WQ_WAVES) void gemm_wstream_fp8(
 #pragma unroll
     for (int q = 0; q < WQ_AQ; ++q) ws_dma<false>(r, dst + q * 1024, a_voff[q], kbi * 128);
   };
-  auto issue_s = [&](int stage, int ks) __attribute__((always_inline)) {  // the stage's row scales
+  auto issue_s = [&](int stage, int ks) __attribute__((always_inline)) {  // the stage's row and weight scales
     const int kbi = blk(ks, a_rot);
     const __amdgpu_buffer_rsrc_t rs = ws_rsrc(s_base, WS_RANGE);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -221,11 +236,15 @@ __global__ __launch_bounds__(64 * WQ_WAVES) void gemm_wstream_fp8(
   const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   // issue(m) runs after the MFMAs of row group m: the step's loads go out between its MFMAs
   // instead of in one burst before them.
-  auto compute = [&](int st, float sw0, float sw1, auto&& issue) __attribute__((always_inline)) {
+  auto compute = [&](int st, auto&& issue) __attribute__((always_inline)) {
     const char* As = lds + st * WQ_A;
     const char* Bs = wslab + st * WQ_SLAB;
-    // tile row 32 m + l32's scale: wave m's area holds rows 32 m .. 32 m + 31
-    const float* sxs = reinterpret_cast<const float*>(lds + WQ_SX0 + st * WQ_SX) + l32;
+    // tile row 32 m + l32's scale: wave m's area holds rows 32 m .. 32 m + 31; the weight scales
+    // are the first word of waves 4 and 5's areas (mode 1: the one of this wave's half)
+    const float* sxa = reinterpret_cast<const float*>(lds + WQ_SX0 + st * WQ_SX);
+    const float* sxs = sxa + l32;
+    const float sw0 = sxa[(MODE == 0 ? 4 : 4 + (wave >> 2)) * 64];
+    const float sw1 = MODE == 0 ? sxa[5 * 64] : sw0;
     const i32x8 b0 = ws_frag32(Bs, foff[0][0], foff[0][1]);
     const i32x8 b1 = ws_frag32(Bs, foff[1][0], foff[1][1]);
     i32x8 a0 = ws_frag32(As, foff[0][0], foff[0][1]);
@@ -253,22 +272,6 @@ __global__ __launch_bounds__(64 * WQ_WAVES) void gemm_wstream_fp8(
     }
     promote(WQ_NM - 1, p[(WQ_NM - 1) & 1], sx_prev);
   };
-  // weight scales of the compute cursor's item: mode 0 the 128x128 block row of W1 and of W3
-  // holding the item's h-columns, mode 1 the W2 block row of this wave's 32 output columns
-  const float *wsc0 = nullptr, *wsc1 = nullptr;
-  auto c_set = [&](const WsItem& d) __attribute__((always_inline)) {
-    if (MODE == 0) {
-      const size_t nb = I / 128;
-      wsc0 = (d.sh ? ssa : sa + (size_t)d.expert * nb * nk) + (size_t)d.nt * nk;
-      wsc1 = (d.sh ? ssb : sb_ + (size_t)d.expert * nb * nk) + (size_t)d.nt * nk;
-    } else {
-      const size_t nb = D / 128;
-      const int b = d.nt * 2 + (wave >> 2);
-      wsc0 = (d.sh ? ssa : sa + (size_t)d.expert * nb * nk) + (size_t)b * nk;
-      wsc1 = wsc0;
-    }
-  };
-
   // ---- epilogues. A lane holds tile row 32 m + l32 and, for each jj = q / 4, the four
   // consecutive weight rows 8 jj + 4 lh .. + 3 of the wave, stored as one 4-byte word (mode 0:
   // codes of h-columns 16 wave + 8 jj + 4 lh ..) or 8-byte word (mode 1: bf16 of output columns
@@ -331,17 +334,16 @@ __global__ __launch_bounds__(64 * WQ_WAVES) void gemm_wstream_fp8(
     }
   };
 
-  // Step n of the item, compute cursor at block ks_c of it, stage and slab of step n in slot st:
-  // request stage and slab n + 2 (at step ks of the load cursor's item) and multiply.
+  // Step n of the item, stage and slab of step n in slot st: request stage and slab n + 2 (at
+  // step ks of the load cursor's item) and multiply.
   int st = 0;
-  int c_rot = 0;
   auto step = [&](int ks, int ks_c) __attribute__((always_inline)) {
-    wait_vmcnt<WQ_AQ + 1 + WQ_BQ>();  // loads after slab n: stage n + 1 (+ its row scales), slab n + 1
+    (void)ks_c;
+    wait_vmcnt<WQ_AQ + 1 + WQ_BQ>();  // loads after slab n: stage n + 1 (+ its scales), slab n + 1
     wait_lgkm0();
     barrier_only();
     const int s2 = st == 0 ? 2 : st - 1;
-    const int kbc = blk(ks_c, c_rot);
-    compute(st, wsc0[kbc], wsc1[kbc], [&](int m) __attribute__((always_inline)) {
+    compute(st, [&](int m) __attribute__((always_inline)) {
       using std::integral_constant;
       if (m == 0) issue_a(s2, ks);
       if (m == 1) {
@@ -392,8 +394,6 @@ __global__ __launch_bounds__(64 * WQ_WAVES) void gemm_wstream_fp8(
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[m][q] = 0.f;
     const WsItem next = item_of(i + 1);
-    c_set(cur);
-    c_rot = cur.rot;
     body();
     tail(next);
     // the accumulators are final here: keeps the compiler from sinking the tail's MFMAs into the
