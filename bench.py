@@ -179,16 +179,26 @@ def step_units(shape, counts):
     return nbytes, router_flops + expert_flops, t_mfma
 
 
-def measure(shape, tens, blk, steps, warmup, dense):
+def measure(shape, tens, blk, steps, warmup, dense, fused=False):
     """Warm up, time `steps` steps (HIP events around the dominant kernel's launches inside the
     timed region), after an untimed pass of the same length with events around every launch that
-    gives the per-kernel breakdown and picks the dominant kernel."""
+    gives the per-kernel breakdown and picks the dominant kernel. fused: each step is one
+    moe_forward_fused launch instead of moe_forward."""
     import torch
 
     from mixture_experts_layer_14_amd import moe
 
     out = torch.empty_like(tens.x)
     stream = torch.cuda.current_stream()
+    if fused:
+        plain = blk
+
+        class _Fused:
+            ws_view = plain.ws_view
+
+            def forward(self, x, o):
+                moe.forward_fused(plain.cfg, plain.wts, x, o, plain.ws)
+        blk = _Fused()
     for _ in range(warmup):
         blk.forward(tens.x, out)
     torch.cuda.synchronize()
@@ -225,6 +235,8 @@ def measure(shape, tens, blk, steps, warmup, dense):
     dom_cnt, dom_tot = kt_dom[dom]
     dom_ms = dom_tot / dom_cnt
     kind = "gemm1" if ("gemm1" in dom or "<0" in dom) else ("gemm2" if ("gemm2" in dom or "<1" in dom) else None)
+    if fused:  # one kernel is the whole step: its roof is every algorithmic byte of the step
+        kind = None
     roof = None
     if kind:
         nbytes, flops = units[kind]
@@ -325,6 +337,15 @@ def main():
     }
     if not dense:
         rec["step"] = {k: v for k, v in workload_summary(shape, m).items() if k not in ("dominant", "kernels_ms")}
+
+    # The fused single-launch decode on the same inputs (moe_forward_fused), against the headline's
+    # separate launches.
+    if not dense and not args.no_workloads and args.workload == "decode_bf16":
+        print("[bench] decode_bf16: the fused single launch", file=sys.stderr, flush=True)
+        mf = measure(shape, tens, blk, args.steps, args.warmup, False, fused=True)
+        fs = workload_summary(shape, mf)
+        rec["fused_decode"] = {k: fs[k] for k in ("ms_per_step", "tokens_per_s", "hbm_frac", "kernels_ms")}
+        rec["fused_decode"]["vs_separate_launches"] = round(ms / mf["ms"], 4)
 
     # The other workloads of the block, timed in the same run (not the headline value): the tiny
     # fp32 block, the 4096-token bf16 prefill (HBM-bound), the skewed 4096-token prefill and the

@@ -145,6 +145,19 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* idx, int64_t T, in
 moe_status moe_forward(const moe_config* cfg, const moe_weights* wts, const void* x, int64_t T,
                        void* out, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward in a single launch, for decode-sized bf16 batches (1 to 32
+ * tokens, at most 256 routed experts): router logits, selection, dispatch,
+ * gate/up + SwiGLU, down projection and combine run as phases of one
+ * cooperative grid separated by grid-wide barriers (hipLaunchCooperativeKernel:
+ * every block of the grid is resident at once). Each phase runs the device code
+ * of moe_forward's separate kernels, so the output equals moe_forward's bit for
+ * bit, and the workspace is the same (moe_workspace_size, moe_workspace_layout).
+ * The pages' MoE block and router as for moe_forward. Errors as moe_forward,
+ * plus MOE_ERR_UNSUPPORTED for other dtypes or sizes (checked on the host before
+ * any launch), and MOE_ERR_HIP when the cooperative launch is refused. */
+moe_status moe_forward_fused(const moe_config* cfg, const moe_weights* wts, const void* x, int64_t T,
+                             void* out, void* ws, size_t ws_bytes, void* stream);
+
 /* moe_forward without a caller workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc). Same arguments, results and errors as moe_forward,

@@ -417,6 +417,49 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* idx, int64_t T, in
                     "dispatch");
 }
 
+}  // extern "C"
+
+namespace {
+// The host-side checks of a block forward (T > 0): tensors present and aligned, configuration,
+// workspace size.
+moe_status check_forward(const moe_config* cfg, const moe_weights* wts, const void* x, const void* out,
+                         const moe::Dims& d, const Layout& L, const void* ws, size_t ws_bytes) {
+  if (!x || !out || !wts->w_gate || !wts->w1 || !wts->w3 || !wts->w2 || !wts->ws1 || !wts->ws3 || !wts->ws2)
+    return fail(MOE_ERR_ARG, "NULL tensor argument");
+  if (d.dtype == MOE_FP8 && (!wts->s1 || !wts->s3 || !wts->s2 || !wts->ss1 || !wts->ss3 || !wts->ss2))
+    return fail(MOE_ERR_ARG, "fp8 weights need their block scales");
+  const void* ptrs[] = {x, out, wts->w_gate, wts->bias, wts->w1, wts->w3, wts->w2, wts->ws1, wts->ws3, wts->ws2};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(MOE_ERR_ARG, "device pointers must be 16-byte aligned");
+  if (wts->bias && d.G > 1 && d.E / d.G < 2)
+    return fail(MOE_ERR_CONFIG, "top-2 group score needs 2 experts per group");
+  return check_ws(L, ws, ws_bytes);
+}
+
+// The expert-GEMM view of a forward workspace.
+moe::Act forward_act(const moe::Dims& d, const Layout& L, const void* x, void* ws) {
+  const bool fp8 = d.dtype == MOE_FP8;
+  moe::Act act;
+  act.x = fp8 ? static_cast<const void*>(at<uint8_t>(ws, L.pub.xq)) : x;
+  act.x_scale = fp8 ? at<float>(ws, L.pub.x_scale) : nullptr;
+  act.row_token = at<int32_t>(ws, L.pub.row_token);
+  act.offsets = at<int32_t>(ws, L.pub.offsets);
+  act.meta = at<int32_t>(ws, L.meta);
+  act.tiles_skinny = at<Tile>(ws, L.tiles_s);
+  act.tiles_wide = at<Tile>(ws, L.tiles_w);
+  act.tiles_wide2 = at<Tile>(ws, L.tiles_w2);
+  act.h_routed = at<void>(ws, L.pub.h_routed);
+  act.h_shared = at<void>(ws, L.pub.h_shared);
+  act.h_scale = fp8 ? at<float>(ws, L.pub.h_scale) : nullptr;
+  act.h_shared_scale = fp8 ? at<float>(ws, L.pub.h_shared_scale) : nullptr;
+  act.o_routed = at<void>(ws, L.pub.o_routed);
+  act.o_shared = at<void>(ws, L.pub.o_shared);
+  return act;
+}
+}  // namespace
+
+extern "C" {
+
 moe_status moe_forward(const moe_config* cfg, const moe_weights* wts, const void* x, int64_t T, void* out, void* ws,
                        size_t ws_bytes, void* stream) {
   moe::Dims d;
@@ -424,18 +467,9 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wts, const void
   if (st != MOE_OK) return st;
   if (!wts) return fail(MOE_ERR_ARG, "wts is NULL");
   if (T == 0) return MOE_OK;
-  if (!x || !out || !wts->w_gate || !wts->w1 || !wts->w3 || !wts->w2 || !wts->ws1 || !wts->ws3 || !wts->ws2)
-    return fail(MOE_ERR_ARG, "NULL tensor argument");
-  const bool fp8 = d.dtype == MOE_FP8;
-  if (fp8 && (!wts->s1 || !wts->s3 || !wts->s2 || !wts->ss1 || !wts->ss3 || !wts->ss2))
-    return fail(MOE_ERR_ARG, "fp8 weights need their block scales");
-  const void* ptrs[] = {x, out, wts->w_gate, wts->bias, wts->w1, wts->w3, wts->w2, wts->ws1, wts->ws3, wts->ws2};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return fail(MOE_ERR_ARG, "device pointers must be 16-byte aligned");
-  if (wts->bias && d.G > 1 && d.E / d.G < 2)
-    return fail(MOE_ERR_CONFIG, "top-2 group score needs 2 experts per group");
   Layout L = plan(d);
-  if ((st = check_ws(L, ws, ws_bytes)) != MOE_OK) return st;
+  if ((st = check_forward(cfg, wts, x, out, d, L, ws, ws_bytes)) != MOE_OK) return st;
+  const bool fp8 = d.dtype == MOE_FP8;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   int32_t* idx = at<int32_t>(ws, L.pub.idx);
@@ -463,23 +497,32 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wts, const void
     return st;
   moe::ExpertPtrs ep{wts->w1, wts->w3, wts->w2, wts->ws1, wts->ws3, wts->ws2,
                      wts->s1, wts->s3, wts->s2, wts->ss1, wts->ss3, wts->ss2};
-  moe::Act act;
-  act.x = fp8 ? static_cast<const void*>(at<uint8_t>(ws, L.pub.xq)) : x;
-  act.x_scale = fp8 ? at<float>(ws, L.pub.x_scale) : nullptr;
-  act.row_token = row_token;
-  act.offsets = offsets;
-  act.meta = meta;
-  act.tiles_skinny = at<Tile>(ws, L.tiles_s);
-  act.tiles_wide = at<Tile>(ws, L.tiles_w);
-  act.tiles_wide2 = at<Tile>(ws, L.tiles_w2);
-  act.h_routed = at<void>(ws, L.pub.h_routed);
-  act.h_shared = at<void>(ws, L.pub.h_shared);
-  act.h_scale = fp8 ? at<float>(ws, L.pub.h_scale) : nullptr;
-  act.h_shared_scale = fp8 ? at<float>(ws, L.pub.h_shared_scale) : nullptr;
-  act.o_routed = at<void>(ws, L.pub.o_routed);
-  act.o_shared = at<void>(ws, L.pub.o_shared);
+  const moe::Act act = forward_act(d, L, x, ws);
   if ((st = hip_status(moe::launch_experts(d, ep, act, s), "experts")) != MOE_OK) return st;
   return hip_status(moe::launch_combine(d, idx, w, row_of, act.o_routed, act.o_shared, out, s), "combine");
+}
+
+moe_status moe_forward_fused(const moe_config* cfg, const moe_weights* wts, const void* x, int64_t T, void* out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  moe::Dims d;
+  moe_status st = check_config(cfg, T, &d);
+  if (st != MOE_OK) return st;
+  if (!wts) return fail(MOE_ERR_ARG, "wts is NULL");
+  if (T == 0) return MOE_OK;
+  if (!moe::decode_fused_ok(d))
+    return fail(MOE_ERR_UNSUPPORTED, "the fused decode takes bf16 blocks of 1 to " + std::to_string(moe::kFusedMaxT) +
+                                         " tokens and at most " + std::to_string(moe::kFusedMaxE) + " experts");
+  Layout L = plan(d);
+  if ((st = check_forward(cfg, wts, x, out, d, L, ws, ws_bytes)) != MOE_OK) return st;
+  moe::ExpertPtrs ep{wts->w1, wts->w3, wts->w2, wts->ws1, wts->ws3, wts->ws2,
+                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  const moe::Act act = forward_act(d, L, x, ws);
+  return hip_status(moe::launch_decode_fused(d, ep, wts->w_gate, wts->bias, cfg->route_scale,
+                                             cfg->score_func == MOE_SCORE_SOFTMAX, x, at<double>(ws, L.zpart), L.nsplit,
+                                             at<int32_t>(ws, L.pub.idx), at<float>(ws, L.pub.w),
+                                             at<int32_t>(ws, L.pub.counts), act, at<int32_t>(ws, L.pub.row_of), out,
+                                             static_cast<hipStream_t>(stream)),
+                    "fused decode");
 }
 
 moe_status moe_forward_static(const moe_config* cfg, const moe_weights* wts, const void* x, int64_t T, void* out,

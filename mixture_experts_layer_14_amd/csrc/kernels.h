@@ -123,6 +123,16 @@ hipError_t launch_wstream_fp8(const Dims& d, const ExpertPtrs& w, const Act& a, 
 bool wide_ok(const Dims& d);
 hipError_t launch_wide_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s);
 
+// ---- the fused single-launch decode (bf16, at most kFusedMaxT tokens and kFusedMaxE experts)
+constexpr int kFusedMaxT = 32;
+constexpr int kFusedMaxE = 256;
+bool decode_fused_ok(const Dims& d);
+// Router logits' k-slice length for nsplit slices (whole 32-element chunks).
+int router_kslice(const Dims& d, int nsplit);
+hipError_t launch_decode_fused(const Dims& d, const ExpertPtrs& w, const void* w_gate, const float* bias,
+                               float route_scale, bool softmax, const void* x, double* zpart, int nsplit, int32_t* idx,
+                               float* wt, int32_t* counts, const Act& a, int32_t* row_of, void* out, hipStream_t s);
+
 // ---- combine
 hipError_t launch_combine(const Dims& d, const int32_t* idx, const float* w, const int32_t* row_of,
                           const void* o_routed, const void* o_shared, void* out, hipStream_t s);

@@ -26,7 +26,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_CONFIG", -3: "MOE_ERR_WOR
 #: Every function include/moe.h declares.
 EXPORTS = ["moe_workspace_size", "moe_route", "moe_dispatch", "moe_forward", "moe_workspace_layout",
            "moe_status_str", "moe_last_error", "moe_timing_enable", "moe_timing_filter",
-           "moe_timing_report", "moe_ffn_workspace_size", "moe_ffn", "moe_forward_static"]
+           "moe_timing_report", "moe_ffn_workspace_size", "moe_ffn", "moe_forward_static", "moe_forward_fused"]
 
 #: Bytes of the library's static workspace (MOE_STATIC_SCRATCH_BYTES in include/moe.h).
 STATIC_SCRATCH_BYTES = 64 << 20
@@ -78,10 +78,11 @@ def lib() -> ctypes.CDLL:
         L.moe_dispatch.argtypes = [ctypes.POINTER(MoeConfig), vp, i64, vp, vp, vp, vp, vp, sz, vp]
         L.moe_forward.argtypes = [ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeWeights), vp, i64, vp, vp, sz, vp]
         L.moe_forward_static.argtypes = [ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeWeights), vp, i64, vp, vp]
+        L.moe_forward_fused.argtypes = [ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeWeights), vp, i64, vp, vp, sz, vp]
         L.moe_ffn_workspace_size.argtypes = [ctypes.POINTER(FfnConfig), i64, ctypes.POINTER(sz)]
         L.moe_ffn.argtypes = [ctypes.POINTER(FfnConfig), ctypes.POINTER(FfnWeights), vp, i64, vp, vp, sz, vp]
         for f in ["moe_workspace_size", "moe_workspace_layout", "moe_route", "moe_dispatch", "moe_forward",
-                  "moe_ffn_workspace_size", "moe_ffn", "moe_forward_static"]:
+                  "moe_ffn_workspace_size", "moe_ffn", "moe_forward_static", "moe_forward_fused"]:
             getattr(L, f).restype = ctypes.c_int
         L.moe_status_str.argtypes = [ctypes.c_int]
         L.moe_status_str.restype = ctypes.c_char_p
@@ -149,6 +150,13 @@ def forward(cfg: MoeConfig, wts: MoeWeights, x, out, ws, stream=None, tokens: Op
     n = x.shape[0] if tokens is None else tokens
     _check(lib().moe_forward(ctypes.byref(cfg), ctypes.byref(wts), _ptr(x), n, _ptr(out), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+def forward_fused(cfg: MoeConfig, wts: MoeWeights, x, out, ws, stream=None, tokens: Optional[int] = None):
+    """moe_forward in one cooperative launch (bf16, 1 to 32 tokens, at most 256 experts)."""
+    n = x.shape[0] if tokens is None else tokens
+    _check(lib().moe_forward_fused(ctypes.byref(cfg), ctypes.byref(wts), _ptr(x), n, _ptr(out), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)), "moe_forward_fused")
 
 
 def forward_static(cfg: MoeConfig, wts: MoeWeights, x, out, stream=None, tokens: Optional[int] = None):

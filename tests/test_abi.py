@@ -188,3 +188,17 @@ def test_workspace_size_of_zero_tokens(dtype):
     f = moe.FfnConfig(7168, 18432, {"f32": 0, "bf16": 1, "fp8": 2}[dtype])
     size = ctypes.c_size_t()
     assert moe.lib().moe_ffn_workspace_size(ctypes.byref(f), 0, ctypes.byref(size)) == 0
+
+
+def test_fused_decode_refuses_other_shapes_on_the_host():
+    """moe_forward_fused takes bf16 blocks of 1 to 32 tokens with at most 256 experts; anything else
+    is MOE_ERR_UNSUPPORTED before any device call (T = 0 is a no-op)."""
+    L = moe.lib()
+    wts = moe.MoeWeights()
+    n = ctypes.c_size_t(0)
+    for cfg, T in [(cfg_of(), 33), (cfg_of(dtype="fp8"), 16), (cfg_of(dtype="f32"), 16),
+                   (cfg_of(n_experts=512, n_groups=16), 16)]:
+        assert L.moe_forward_fused(ctypes.byref(cfg), ctypes.byref(wts), None, T, None, None, n, None) == -5
+        assert "fused decode" in L.moe_last_error().decode()
+    assert L.moe_forward_fused(ctypes.byref(cfg_of()), ctypes.byref(wts), None, 0, None, None, n, None) == 0
+    assert L.moe_forward_fused(ctypes.byref(cfg_of()), None, None, 4, None, None, n, None) == -1
