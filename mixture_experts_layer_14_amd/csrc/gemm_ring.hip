@@ -24,19 +24,6 @@
 
 namespace moe {
 
-#ifndef MOE_RING_BM
-#define MOE_RING_BM 256
-#endif
-#ifndef MOE_RING_BN
-#define MOE_RING_BN 256
-#endif
-#ifndef MOE_RING_BK
-#define MOE_RING_BK 64
-#endif
-#ifndef MOE_RING_STAGES
-#define MOE_RING_STAGES 2
-#endif
-
 constexpr int R_WAVES = 8;
 
 typedef __bf16 bf16x8r_t __attribute__((ext_vector_type(8)));
@@ -201,7 +188,8 @@ __global__ __launch_bounds__(64 * R_WAVES) void gemm_ring_bf16(
   }
 }
 
-constexpr int RBM = MOE_RING_BM, RBN = MOE_RING_BN, RBK = MOE_RING_BK, RST = MOE_RING_STAGES;
+// 256 x 256 tiles, 64-k stages, two stages in flight (128 KB of LDS)
+constexpr int RBM = 256, RBN = 256, RBK = 64, RST = 2;
 
 static size_t ring_lds() { return (size_t)RST * (RBM + RBN) * RBK * 2; }
 
