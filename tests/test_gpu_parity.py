@@ -259,6 +259,29 @@ def test_route_without_bias_uses_group_max():
     route_check(shape, r, np_i32(idx), w.cpu().numpy())
 
 
+@pytest.mark.parametrize("T,D,E,G,Gk,K", [(4000, 7168, 256, 8, 4, 8), (1100, 1152, 72, 8, 4, 6),
+                                           (1024, 512, 320, 8, 4, 8)])
+def test_route_large_batch_tiles(T, D, E, G, Gk, K):
+    """moe_route on the large-batch logits tiles (64 tokens x 256 experts, 64-k stages through
+    LDS) at their edges: k-slices of an odd number of 32-k chunks, whose last stage is half empty
+    (the full router at 4000 tokens: 5 slices of 45 chunks and one of 44; 1152 dims: 8 slices of 5
+    chunks and a last of 1), a last token tile partly filled, and expert counts that leave part of
+    an expert tile empty (72; 320 = one full tile and one of 64). Routing on every token."""
+    shape = inputs.WORKLOADS["prefill_bf16"].replace(name=f"route_{T}x{D}x{E}", tokens=T, dim=D, n_experts=E,
+                                                     n_groups=G, topk_groups=Gk, topk=K, inter=128)
+    say(f"[route/large batch] T={T} D={D} E={E}")
+    tens = inputs.generate(shape, seed=12, device=DEV)
+    cfg = moe.config(shape)
+    ws = torch.empty(moe.workspace_size(cfg, T), dtype=torch.uint8, device=DEV)
+    idx = torch.empty(T, K, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, K, dtype=torch.float32, device=DEV)
+    moe.route(cfg, tens.w_gate, tens.bias, tens.x, idx, w, ws)
+    torch.cuda.synchronize()
+    r = O.route(shape, exact(tens.x), exact(tens.w_gate), bias_np(tens))
+    _, rep = route_check(shape, r, np_i32(idx), w.cpu().numpy())
+    say(f"  route {rep}")
+
+
 @pytest.mark.parametrize("T,E,K", [(1, 256, 8), (1000, 256, 8), (3000, 64, 6), (513, 16, 4)])
 def test_dispatch_standalone(T, E, K):
     shape = inputs.WORKLOADS["decode_bf16"].replace(n_experts=E, topk=K, n_groups=8 if E >= 64 else 4,
