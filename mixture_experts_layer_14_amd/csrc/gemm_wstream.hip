@@ -28,10 +28,14 @@
 // slab n + 1 and stage n + 2 in flight (activations first measured 1-2% slower). The step sequence runs on across the block's items without draining: an item's last
 // steps request the next item's first stages. A ragged tile multiplies only its live 32-row groups.
 //
-// The dense layer (no routed experts, every M-tile full) takes 256-row M-tiles instead: the same
-// weight slabs, two 32 KB activation stages issued one step ahead (first in their step), 256
-// accumulators per wave, a third fewer bytes per flop through the load path. With routed experts
-// the 128-row tiles measured faster, hot experts of several tiles included.
+// Tile kinds. The down projection runs on the 128-row tile list (kTk128; a dense layer of 1024
+// tokens or more on the 256-row list with steps over all 256 rows, kTk256: the same weight slabs,
+// two 32 KB activation stages issued one step ahead and first in their step, 256 accumulators per
+// wave). Gate/up runs on the 256-row tile list with each tile as one or two 128-row halves
+// (kTkPair): a tile of an expert with more than 128 rows alternates half-steps between its halves,
+// both multiplying the same weight slab, so each weight byte is loaded once per 256 rows while the
+// activation ring keeps its four 16 KB stages; a tile of at most 128 rows runs as kTk128 does.
+// The per-expert tile height thus follows the expert's row count.
 //
 // Steps come in groups of four (the activation stages rotate with the group), so an item's steps
 // (dim / 64 or inter / 64) must be a multiple of four; the epilogue and the accumulator reset run
@@ -49,19 +53,24 @@ constexpr int WS_BK = 64;                                            // k per st
 constexpr int WS_NB = 3;                                             // weight slabs per wave
 constexpr int WS_SLAB = WS_WROWS * WS_BK * 2;                        // 8 KB
 constexpr int WS_BQ = WS_WROWS / 8;                                  // weight loads per wave and step
-// per M-tile height BM (128, or 256 for the dense layer): activation stages (4 of 16 KB, or 2 of
-// 32 KB), loads per wave and step, 32-row groups; the LDS holds the stages and then the slabs
-template <int BM>
+// Tile kinds: the 128-row tile list; the 256-row tile list with a step over all 256 rows; the
+// 256-row tile list with each tile run as one or two 128-row halves that share the weight slabs.
+constexpr int kTk128 = 0, kTk256 = 1, kTkPair = 2;
+// per tile kind: rows of an activation stage, stages (4 of 16 KB, or 2 of 32 KB), loads per wave
+// and step, 32-row groups, halves; the LDS holds the stages and then the slabs
+template <int TK>
 struct WsDims {
-  static constexpr int NA = BM == 128 ? 4 : 2;
-  static constexpr int A_STAGE = BM * WS_BK * 2;
-  static constexpr int AQ = BM / 8 / WS_WAVES;
-  static constexpr int NM = BM / 32;
+  static constexpr int ROWS = TK == kTk256 ? 256 : 128;
+  static constexpr int NA = TK == kTk256 ? 2 : 4;
+  static constexpr int A_STAGE = ROWS * WS_BK * 2;
+  static constexpr int AQ = ROWS / 8 / WS_WAVES;
+  static constexpr int NM = ROWS / 32;
+  static constexpr int NH = TK == kTkPair ? 2 : 1;
   static constexpr int B0 = NA * A_STAGE;
   static constexpr size_t LDS = (size_t)B0 + (size_t)WS_WAVES * WS_NB * WS_SLAB;  // 160 KB
 };
-static_assert(WsDims<128>::LDS == WsDims<256>::LDS, "both tile heights fill the LDS alike");
-constexpr size_t WS_LDS = WsDims<128>::LDS;
+static_assert(WsDims<kTk128>::LDS == WsDims<kTk256>::LDS, "both stage heights fill the LDS alike");
+constexpr size_t WS_LDS = WsDims<kTk128>::LDS;
 
 typedef __bf16 bf16x8w_t __attribute__((ext_vector_type(8)));
 
@@ -70,11 +79,9 @@ MOE_DEV f32x16 mfma32w(i32x4 a, i32x4 b, f32x16 c) {
                                                  0, 0, 0);
 }
 
-// NT: every weight load nontemporal (else only the tiles of single-M-tile experts). BM: rows per
-// M-tile, 128 (the tile list of 128-row tiles) or 256 (that of 256-row tiles: the dense layer,
-// whose tiles are full; its activation stages are then two, issued one step ahead and first in
-// each step, since the LDS holds only two 32 KB stages beside the slabs).
-template <int MODE, bool NT, int BM>
+// NT: every weight load nontemporal (else only the tiles of single-M-tile experts). TK: the tile
+// kind (kTk128, kTk256 or kTkPair, above).
+template <int MODE, bool NT, int TK>
 __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
     const bf16_t* __restrict__ act_x, const bf16_t* __restrict__ h_routed_in, const bf16_t* __restrict__ h_shared_in,
     const int32_t* __restrict__ row_token, const int32_t* __restrict__ offsets, const Tile* __restrict__ tiles,
@@ -82,16 +89,17 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
     const bf16_t* __restrict__ wsa, const bf16_t* __restrict__ wsb, bf16_t* __restrict__ out_routed,
     bf16_t* __restrict__ out_shared, int T, int D, int I, int S, int E) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  using W = WsDims<BM>;
-  constexpr int WS_BM = BM, WS_NA = W::NA, WS_A_STAGE = W::A_STAGE, WS_AQ = W::AQ, WS_NM = W::NM, WS_B0 = W::B0;
+  using W = WsDims<TK>;
+  constexpr int WS_NA = W::NA, WS_A_STAGE = W::A_STAGE, WS_AQ = W::AQ, WS_NM = W::NM, WS_NH = W::NH, WS_B0 = W::B0;
+  constexpr int LIST = TK == kTk128 ? kWideBM : kWideBM2;  // the tile list's rows per tile
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, lh = lane >> 5;
   constexpr int HN = MODE == 0 ? 128 : 256;  // output columns per item
   const int per_r = MODE == 0 ? I / HN : D / HN;
   const int per_s = MODE == 0 ? S / HN : D / HN;
-  const int nr = meta[BM == 128 ? 2 : 5];
-  const int items = nr * per_r + (meta[BM == 128 ? 3 : 6] - nr) * per_s;
+  const int nr = meta[LIST == kWideBM ? 2 : 5];
+  const int items = nr * per_r + (meta[LIST == kWideBM ? 3 : 6] - nr) * per_s;
   // this block's items: xcd * chunk + slot + i * per_xcd for i < mine (an XCD's blocks share a range)
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
   const int chunk = (items + 7) >> 3;
@@ -105,7 +113,7 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
     d.live = i < mine;
     d.row0 = 0, d.nrows = 0, d.nt = 0, d.expert = 0, d.rot = 0, d.sh = false, d.solo = false;
     if (d.live) {
-      const WideItem it = wide_item<WS_BM>(xcd * chunk + slot + i * per_xcd, tiles, nr, offsets, T, E, per_r, per_s);
+      const WideItem it = wide_item<LIST>(xcd * chunk + slot + i * per_xcd, tiles, nr, offsets, T, E, per_r, per_s);
       d.row0 = it.tl.row0;
       d.nrows = it.tl.nrows;
       d.nt = it.nt;
@@ -177,50 +185,62 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
     issue_b(std::integral_constant<int, 0>{}, std::integral_constant<int, WS_BQ>{}, slot_b, ks);
   };
 
-  // ---- activation rows: instruction q of this wave fills tile rows RW wave + 8 q + lane / 8 (RW =
-  // BM / 4 rows per wave); mode 0: the token of tile row RW wave + lane (lanes < RW, clamped to the
-  // tile), loaded a step before a_set needs it so that waiting for it does not drain the loads in flight
-  constexpr int RW = BM / WS_WAVES;
+  // ---- activation rows: instruction q of this wave fills stage rows RW wave + 8 q + lane / 8 (RW =
+  // rows of a stage / 4); half hh (kTkPair) is tile rows 128 hh .. of the tile. Mode 0: the token of
+  // stage row RW wave + lane (lanes < RW; kTkPair: lanes 32 .. 63 hold half 1's), clamped to the
+  // tile, loaded a step before a_set needs it so that waiting for it does not drain the loads in flight
+  constexpr int RW = W::ROWS / WS_WAVES;
   auto tok_load = [&](const WsItem& d) __attribute__((always_inline)) {
     int t = 0;
     if (MODE == 0 && d.live) {
-      const int r = min(wave * RW + (lane_now() & (RW - 1)), d.nrows - 1);
+      const int ln = lane_now();
+      const int r = min(TK == kTkPair ? (ln >> 5) * 128 + wave * 32 + (ln & 31) : wave * RW + (ln & (RW - 1)),
+                        d.nrows - 1);
       t = d.sh ? d.row0 + r : row_token[d.row0 + r];
     }
     return t;
   };
   const bf16_t* a_base;
-  int a_voff[WS_AQ], a_rot;
+  int a_voff[WS_NH][WS_AQ], a_rot;
   auto a_set = [&](const WsItem& d, int tok_mine) __attribute__((always_inline)) {
     const int ln = lane_now();
-    const int a_row = wave * RW + (ln >> 3);  // tile row of this lane in instruction 0
-    const int a_c0 = (ln & 7) ^ (ln >> 3);     // its source chunk, xor (q & 3) for instruction q
+    const int a_c0 = (ln & 7) ^ (ln >> 3);  // the source chunk of instruction 0, xor (q & 3) for instruction q
     a_base = MODE == 0 ? act_x : (d.sh ? h_shared_in : h_routed_in);
     a_rot = d.rot;
     const int row_bytes = (MODE == 0 ? D : (d.sh ? S : I)) * 2;
 #pragma unroll
-    for (int q = 0; q < WS_AQ; ++q) {
-      const int c16 = (a_c0 ^ (q & 3)) << 4;
-      int off = WS_OOB;
-      if (MODE == 0) {
-        const int tok = __shfl(tok_mine, q * 8 + (ln >> 3));
-        if (d.live && a_row < d.nrows - q * 8) off = tok * row_bytes + c16;
-      } else {
-        if (d.live && a_row < d.nrows - q * 8) off = (d.row0 + a_row + q * 8) * row_bytes + c16;
+    for (int hh = 0; hh < WS_NH; ++hh) {
+      const int a_row = hh * 128 + wave * RW + (ln >> 3);  // tile row of this lane in instruction 0
+#pragma unroll
+      for (int q = 0; q < WS_AQ; ++q) {
+        const int c16 = (a_c0 ^ (q & 3)) << 4;
+        int off = WS_OOB;
+        if (MODE == 0) {
+          const int tok = __shfl(tok_mine, hh * 32 + q * 8 + (ln >> 3));
+          if (d.live && a_row < d.nrows - q * 8) off = tok * row_bytes + c16;
+        } else {
+          if (d.live && a_row < d.nrows - q * 8) off = (d.row0 + a_row + q * 8) * row_bytes + c16;
+        }
+        a_voff[hh][q] = off;
       }
-      a_voff[q] = off;
     }
   };
-  auto issue_a = [&](int stage, int ks) __attribute__((always_inline)) {
+  // stage rows of half hh at step ks
+  auto issue_a = [&](int stage, int ks, int hh) __attribute__((always_inline)) {
     const int kb = kbytes(ks, a_rot);
     const __amdgpu_buffer_rsrc_t r = ws_rsrc(a_base, WS_RANGE);
     char* dst = lds + stage * WS_A_STAGE + wave * WS_AQ * 1024;
+    if (WS_NH == 1 || hh == 0) {
 #pragma unroll
-    for (int q = 0; q < WS_AQ; ++q) ws_dma<false>(r, dst + q * 1024, a_voff[q], kb);
+      for (int q = 0; q < WS_AQ; ++q) ws_dma<false>(r, dst + q * 1024, a_voff[0][q], kb);
+    } else {
+#pragma unroll
+      for (int q = 0; q < WS_AQ; ++q) ws_dma<false>(r, dst + q * 1024, a_voff[WS_NH - 1][q], kb);
+    }
   };
 
-  // ---- multiply one step: acc[m][s] += A(rows 32 m ..) W(wave rows 32 s ..)^T over 64 k
-  f32x16 acc[WS_NM][2];
+  // ---- multiply one step: acc[h][m][s] += A(rows 128 h + 32 m ..) W(wave rows 32 s ..)^T over 64 k
+  f32x16 acc[WS_NH][WS_NM][2];
   // fragment k-chunk kk * 2 + lh of row l32 (+ 32 per row group): one per-lane offset per kk
   int foff[WS_BK / 16];
 #pragma unroll
@@ -229,8 +249,9 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
   // scheduling groups spread those reads between the MFMAs.
   // issue(kk) runs after the MFMAs of k-step kk: the step's loads go out between its MFMAs
   // instead of in one burst before them.
-  auto compute = [&](auto nm, int stage, int slot_b, auto&& issue) __attribute__((always_inline)) {
+  auto compute = [&](auto nm, auto hc, int stage, int slot_b, auto&& issue) __attribute__((always_inline)) {
     constexpr int NM = decltype(nm)::value;
+    constexpr int H = decltype(hc)::value;
     constexpr int KK = WS_BK / 16;
     const char* As = lds + stage * WS_A_STAGE;
     const char* Bs = wslab + slot_b * WS_SLAB;
@@ -249,8 +270,8 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
       if (kk + 1 < KK) load(kk + 1, cb ^ 1);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        acc[m][0] = mfma32w(fa[cb][m], fb[cb][0], acc[m][0]);
-        acc[m][1] = mfma32w(fa[cb][m], fb[cb][1], acc[m][1]);
+        acc[H][m][0] = mfma32w(fa[cb][m], fb[cb][0], acc[H][m][0]);
+        acc[H][m][1] = mfma32w(fa[cb][m], fb[cb][1], acc[H][m][1]);
       }
       issue(kk);
       if (kk + 1 < KK) {
@@ -265,9 +286,9 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
       }
     }
   };
-  // accumulator element q of lane: row 32 m + 8 (q / 4) + 4 lh + q % 4, weight row 32 s + l32 of the
-  // wave. Stores go through a buffer resource spanning the item's rows, so rows past the tile's end
-  // fall outside it and are dropped, and each store needs one offset register.
+  // accumulator element q of lane: row 128 h + 32 m + 8 (q / 4) + 4 lh + q % 4, weight row 32 s + l32
+  // of the wave. Stores go through a buffer resource spanning the item's rows, so rows past the
+  // tile's end fall outside it and are dropped, and each store needs one offset register.
   auto epilogue = [&](const WsItem& d) __attribute__((always_inline)) {
     const int ld = MODE == 0 ? (d.sh ? S : I) : D;
     const __amdgpu_buffer_rsrc_t o = ws_rsrc((d.sh ? out_shared : out_routed) + (size_t)d.row0 * ld, d.nrows * ld * 2);
@@ -275,45 +296,56 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
     const int vbase = ((ln >> 5) * 4 * ld + d.nt * HN + wave * (MODE == 0 ? 32 : 64) + (ln & 31)) * 2;
     const int row_bytes = ld * 2;
 #pragma unroll
-    for (int m = 0; m < WS_NM; ++m) {
-      if (m * 32 >= d.nrows) continue;
+    for (int h = 0; h < WS_NH; ++h)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int voff = vbase + (m * 32 + (q >> 2) * 8 + (q & 3)) * row_bytes;
-        if (MODE == 0) {
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(silu_mul(acc[m][0][q], acc[m][1][q])), o, voff, 0, 0);
-        } else {
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[m][0][q]), o, voff, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[m][1][q]), o, voff + 64, 0, 0);
+      for (int m = 0; m < WS_NM; ++m) {
+        if (h * 128 + m * 32 >= d.nrows) continue;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int voff = vbase + (h * 128 + m * 32 + (q >> 2) * 8 + (q & 3)) * row_bytes;
+          if (MODE == 0) {
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(silu_mul(acc[h][m][0][q], acc[h][m][1][q])), o, voff, 0,
+                                                  0);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[h][m][0][q]), o, voff, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[h][m][1][q]), o, voff + 64, 0, 0);
+          }
         }
       }
-    }
   };
 
-  // Step j of a group (j = 0..3, step n = 4 g + j of the item, its slab in slot sb): multiply
-  // stage n with slab n, request slab n + 2 (into slot (sb + 2) % 3, at b_ks of the weight cursor's
-  // item) and the activation stage NA - 1 steps ahead (at a_ks of the activation cursor's item).
-  //   BM 128: stage n + 3 into stage (j + 3) % 4, issued after the step's weight loads;
-  //   BM 256: stage n + 1 into stage (j + 1) % 2, issued before them (needed a step later).
-  // Only the item's live 32-row groups (nm of them) are multiplied; the loads do not depend on nm.
-  int sb = 0;  // slot of slab n
-  auto step = [&](auto nm, int j, int a_ks, int b_ks) __attribute__((always_inline)) {
-    if constexpr (BM == 128)
+  // Step j of a group (j = 0..3, step n = 4 g + j of the block's step sequence): multiply
+  // activation stage n with the slab in slot sb, request loads of the slab two k-steps ahead (at
+  // b_ks of the weight cursor's item, into slot (sb + 2) % 3) and the activation stage NA - 1 steps
+  // ahead (half ah at k-step ak of the activation cursor's item).
+  //   kTk128, kTkPair: stage n + 3 into stage (j + 3) % 4, issued after the step's weight loads;
+  //   kTk256: stage n + 1 into stage (j + 1) % 2, issued before them (needed a step later).
+  // kTkPair runs a tile of more than 128 rows as half-steps (half 0, then half 1 of each k-step,
+  // both on that k-step's slab), each issuing half of a slab's loads: 8 loads where a step issues
+  // 12. The wait leaves at most 16 younger loads in flight, which holds under either pattern and
+  // wherever one follows the other. Only the live 32-row groups (nm of them) are multiplied; the
+  // loads do not depend on nm.
+  using std::integral_constant;
+  using H0 = integral_constant<int, 0>;
+  using H1 = integral_constant<int, 1>;
+  int sb = 0;  // slot of the slab in use
+  // a whole k-step (every tile of kTk128 and kTk256, the tiles of at most 128 rows of kTkPair)
+  auto step = [&](auto nm, int j, int ak, int ah, int b_ks) __attribute__((always_inline)) {
+    if constexpr (TK != kTk256)
       wait_vmcnt<2 * WS_AQ + WS_BQ>();  // loads after slab n: stage n + 1, slab n + 1, stage n + 2
     else
       wait_vmcnt<WS_BQ>();  // loads after stage n and slab n: slab n + 1
     wait_lgkm0();
     barrier_only();
     const int sbn = sb == 0 ? 2 : sb - 1;
-    compute(nm, j % WS_NA, sb, [&](int kk) __attribute__((always_inline)) {
-      using std::integral_constant;
-      if constexpr (BM == 128) {
+    compute(nm, H0{}, j % WS_NA, sb, [&](int kk) __attribute__((always_inline)) {
+      if constexpr (TK != kTk256) {
         if (kk == 0) issue_b(integral_constant<int, 0>{}, integral_constant<int, 3>{}, sbn, b_ks);
         if (kk == 1) issue_b(integral_constant<int, 3>{}, integral_constant<int, 6>{}, sbn, b_ks);
         if (kk == 2) issue_b(integral_constant<int, 6>{}, integral_constant<int, WS_BQ>{}, sbn, b_ks);
-        if (kk == 3) issue_a((j + 3) & 3, a_ks);
+        if (kk == 3) issue_a((j + 3) & 3, ak, ah);
       } else {
-        if (kk == 0) issue_a((j + 1) & 1, a_ks);
+        if (kk == 0) issue_a((j + 1) & 1, ak, 0);
         if (kk == 1) issue_b(integral_constant<int, 0>{}, integral_constant<int, 3>{}, sbn, b_ks);
         if (kk == 2) issue_b(integral_constant<int, 3>{}, integral_constant<int, 6>{}, sbn, b_ks);
         if (kk == 3) issue_b(integral_constant<int, 6>{}, integral_constant<int, WS_BQ>{}, sbn, b_ks);
@@ -321,83 +353,154 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
     });
     sb = sb == 2 ? 0 : sb + 1;
   };
+  // a half-step of kTkPair: half H of the k-step, slab loads 4 H .. 4 H + 3 of step b_ks; the slot
+  // moves on after half 1
+  auto half_step = [&](auto nm, auto hc, int j, int ak, int ah, int b_ks) __attribute__((always_inline)) {
+    constexpr int H = decltype(hc)::value;
+    wait_vmcnt<2 * WS_AQ + WS_BQ>();
+    wait_lgkm0();
+    barrier_only();
+    const int sbn = sb == 0 ? 2 : sb - 1;
+    compute(nm, hc, j, sb, [&](int kk) __attribute__((always_inline)) {
+      if (kk == 0) issue_b(integral_constant<int, 4 * H>{}, integral_constant<int, 4 * H + 2>{}, sbn, b_ks);
+      if (kk == 1) issue_b(integral_constant<int, 4 * H + 2>{}, integral_constant<int, 4 * H + 4>{}, sbn, b_ks);
+      if (kk == 3) issue_a((j + 3) & 3, ak, ah);
+    });
+    if (H == 1) sb = sb == 2 ? 0 : sb + 1;
+  };
+  auto paired = [&](const WsItem& d) __attribute__((always_inline)) {
+    return TK == kTkPair && d.live && d.nrows > 128;
+  };
+  // (half, k-step) of step s of an item
+  auto hk = [](bool pair, int s, int& h, int& k) __attribute__((always_inline)) {
+    h = pair ? (s & 1) : 0;
+    k = pair ? (s >> 1) : s;
+  };
   // One item's steps: the non-final groups (both cursors stay inside the item), then the final
   // group, in which each cursor moves on to the next item once it passes the item's last step.
   auto run_item = [&](auto nm, const WsItem& next) __attribute__((always_inline)) {
     constexpr int LA = WS_NA - 1;  // steps the activation cursor runs ahead
     for (int g = 0; g < nk / 4 - 1; ++g) {
       const int k0 = 4 * g;
-      step(nm, 0, k0 + LA, k0 + 2);
-      step(nm, 1, k0 + LA + 1, k0 + 3);
-      step(nm, 2, k0 + LA + 2, k0 + 4);
-      step(nm, 3, k0 + LA + 3, k0 + 5);
+      step(nm, 0, k0 + LA, 0, k0 + 2);
+      step(nm, 1, k0 + LA + 1, 0, k0 + 3);
+      step(nm, 2, k0 + LA + 2, 0, k0 + 4);
+      step(nm, 3, k0 + LA + 3, 0, k0 + 5);
     }
-    if constexpr (BM == 128) {
+    if constexpr (TK != kTk256) {
+      int h0, k0n, h1, k1n, h2, k2n;  // the next item's first three steps
+      const bool np = paired(next);
+      hk(np, 0, h0, k0n);
+      hk(np, 1, h1, k1n);
+      hk(np, 2, h2, k2n);
       const int tok_next = tok_load(next);
-      step(nm, 0, nk - 1, nk - 2);
+      step(nm, 0, nk - 1, 0, nk - 2);
       a_set(next, tok_next);
-      step(nm, 1, 0, nk - 1);
+      step(nm, 1, k0n, h0, nk - 1);
       b_set(next);
-      step(nm, 2, 1, 0);
-      step(nm, 3, 2, 1);
+      step(nm, 2, k1n, h1, 0);
+      step(nm, 3, k2n, h2, 1);
     } else {
-      step(nm, 0, nk - 3, nk - 2);
+      step(nm, 0, nk - 3, 0, nk - 2);
       const int tok_next = tok_load(next);
-      step(nm, 1, nk - 2, nk - 1);
+      step(nm, 1, nk - 2, 0, nk - 1);
       b_set(next);
-      step(nm, 2, nk - 1, 0);
+      step(nm, 2, nk - 1, 0, 0);
       a_set(next, tok_next);
-      step(nm, 3, 0, 1);
+      step(nm, 3, 0, 0, 1);
     }
   };
+  // A kTkPair tile of more than 128 rows: half-steps 4 g + j = (half 0, k 2g), (half 1, k 2g),
+  // (half 0, k 2g + 1), (half 1, k 2g + 1); half 0 is full, half 1 has nmb live row groups.
+  auto run_pair = [&](auto nmb, const WsItem& next) __attribute__((always_inline)) {
+    constexpr integral_constant<int, WS_NM> full{};
+    for (int g = 0; g < nk / 2 - 1; ++g) {
+      const int k0 = 2 * g;
+      half_step(full, H0{}, 0, k0 + 1, 1, k0 + 2);
+      half_step(nmb, H1{}, 1, k0 + 2, 0, k0 + 2);
+      half_step(full, H0{}, 2, k0 + 2, 1, k0 + 3);
+      half_step(nmb, H1{}, 3, k0 + 3, 0, k0 + 3);
+    }
+    int h0, k0n, h1, k1n, h2, k2n;
+    const bool np = paired(next);
+    hk(np, 0, h0, k0n);
+    hk(np, 1, h1, k1n);
+    hk(np, 2, h2, k2n);
+    const int tok_next = tok_load(next);
+    b_set(next);  // this item's last slab went out in the previous group
+    half_step(full, H0{}, 0, nk - 1, 1, 0);
+    a_set(next, tok_next);
+    half_step(nmb, H1{}, 1, k0n, h0, 0);
+    half_step(full, H0{}, 2, k1n, h1, 1);
+    half_step(nmb, H1{}, 3, k2n, h2, 1);
+  };
 
-  // prologue, in the issue order of the steps before step 0 (weights, then activations): stage 0; slab 0,
-  // stage 1; slab 1, stage 2
+  // prologue, in the issue order of the steps before step 0: kTk128 and kTkPair: stage 0; slab 0,
+  // stage 1; slab 1, stage 2 (weights, then activations); kTk256: slab 0; stage 0; slab 1
   WsItem cur = item_of(0);
   b_set(cur);
   a_set(cur, tok_load(cur));
   wait_vmcnt<0>();
-  if constexpr (BM == 128) {
-    issue_a(0, 0);
+  if constexpr (TK != kTk256) {
+    int h, k;
+    const bool cp = paired(cur);
+    hk(cp, 0, h, k);
+    issue_a(0, k, h);
     issue_b_all(0, 0);
-    issue_a(1, 1);
+    hk(cp, 1, h, k);
+    issue_a(1, k, h);
     issue_b_all(1, 1);
-    issue_a(2, 2);
-  } else {  // slab 0; stage 0; slab 1
+    hk(cp, 2, h, k);
+    issue_a(2, k, h);
+  } else {
     issue_b_all(0, 0);
-    issue_a(0, 0);
+    issue_a(0, 0, 0);
     issue_b_all(1, 1);
   }
 
   for (int i = 0; i < mine; ++i) {
 #pragma unroll
-    for (int m = 0; m < WS_NM; ++m)
+    for (int h = 0; h < WS_NH; ++h)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int m = 0; m < WS_NM; ++m)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) acc[m][t][q] = 0.f;
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) acc[h][m][t][q] = 0.f;
     const WsItem next = item_of(i + 1);
     // a ragged tile multiplies only its live row groups (one code path per count, so the step
     // loop itself has no branches)
     const int nm = __builtin_amdgcn_readfirstlane(min(WS_NM, (cur.nrows + 31) >> 5));
-    if constexpr (BM == 128) {
-      if (nm >= 4)
-        run_item(std::integral_constant<int, 4>{}, next);
-      else if (nm == 3)
-        run_item(std::integral_constant<int, 3>{}, next);
-      else if (nm == 2)
-        run_item(std::integral_constant<int, 2>{}, next);
-      else
-        run_item(std::integral_constant<int, 1>{}, next);
-    } else {  // pairs of row groups (only the dense layer's last tile is ragged)
+    if constexpr (TK == kTk256) {  // pairs of row groups (only the dense layer's last tile is ragged)
       if (nm >= 7)
-        run_item(std::integral_constant<int, 8>{}, next);
+        run_item(integral_constant<int, 8>{}, next);
       else if (nm >= 5)
-        run_item(std::integral_constant<int, 6>{}, next);
+        run_item(integral_constant<int, 6>{}, next);
       else if (nm >= 3)
-        run_item(std::integral_constant<int, 4>{}, next);
+        run_item(integral_constant<int, 4>{}, next);
       else
-        run_item(std::integral_constant<int, 2>{}, next);
+        run_item(integral_constant<int, 2>{}, next);
+    } else {
+      bool done = false;
+      if constexpr (TK == kTkPair) {
+        if (paired(cur)) {  // half 1's live row groups, rounded up to 2 or 4
+          if (__builtin_amdgcn_readfirstlane(cur.nrows) > 128 + 64)
+            run_pair(integral_constant<int, 4>{}, next);
+          else
+            run_pair(integral_constant<int, 2>{}, next);
+          done = true;
+        }
+      }
+      if (done) {
+      } else if (nm >= 4) {
+        run_item(integral_constant<int, 4>{}, next);
+      } else if (nm == 3) {
+        run_item(integral_constant<int, 3>{}, next);
+      } else if (nm == 2) {
+        run_item(integral_constant<int, 2>{}, next);
+      } else {
+        run_item(integral_constant<int, 1>{}, next);
+      }
     }
     epilogue(cur);
     cur = next;
@@ -412,38 +515,38 @@ bool wstream_ok(const Dims& d) {
          d.T * d.D * 2 < lim && d.R * d.I * 2 < lim && d.T * d.S * 2 < lim;
 }
 
-template <bool NT, int BM>
+// Gate/up on kTkPair tiles, down on TK1 tiles (kTk128; kTk256 for a large dense layer).
+template <bool NT, int TK1>
 static hipError_t launch_wstream_nt(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s) {
-  const void* k0 = (const void*)gemm_wstream_bf16<0, NT, BM>;
-  const void* k1 = (const void*)gemm_wstream_bf16<1, NT, BM>;
+  const void* k0 = (const void*)gemm_wstream_bf16<0, NT, kTkPair>;
+  const void* k1 = (const void*)gemm_wstream_bf16<1, NT, TK1>;
   hipError_t attr = allow_dynamic_lds(k0, WS_LDS);
   if (attr == hipSuccess) attr = allow_dynamic_lds(k1, WS_LDS);
   if (attr != hipSuccess) return attr;  // never launch with more LDS than the kernel may take
   const int g0 = persistent_grid(k0, 64 * WS_WAVES, WS_LDS) & ~7;
   const int g1 = persistent_grid(k1, 64 * WS_WAVES, WS_LDS) & ~7;
-  const Tile* tiles = BM == 128 ? a.tiles_wide : a.tiles_wide2;
-  MOE_LAUNCH((gemm_wstream_bf16<0, NT, BM>), dim3(g0), dim3(64 * WS_WAVES), WS_LDS, s, (const bf16_t*)a.x, nullptr,
-             nullptr, a.row_token, a.offsets, tiles, a.meta, (const bf16_t*)w.w1, (const bf16_t*)w.w3,
-             (const bf16_t*)w.ws1, (const bf16_t*)w.ws3, (bf16_t*)a.h_routed, (bf16_t*)a.h_shared, (int)d.T, d.D, d.I,
-             d.S, d.E);
-  MOE_LAUNCH((gemm_wstream_bf16<1, NT, BM>), dim3(g1), dim3(64 * WS_WAVES), WS_LDS, s, nullptr,
-             (const bf16_t*)a.h_routed, (const bf16_t*)a.h_shared, a.row_token, a.offsets, tiles, a.meta,
-             (const bf16_t*)w.w2, nullptr, (const bf16_t*)w.ws2, nullptr, (bf16_t*)a.o_routed, (bf16_t*)a.o_shared,
-             (int)d.T, d.D, d.I, d.S, d.E);
+  MOE_LAUNCH((gemm_wstream_bf16<0, NT, kTkPair>), dim3(g0), dim3(64 * WS_WAVES), WS_LDS, s, (const bf16_t*)a.x,
+             nullptr, nullptr, a.row_token, a.offsets, a.tiles_wide2, a.meta, (const bf16_t*)w.w1,
+             (const bf16_t*)w.w3, (const bf16_t*)w.ws1, (const bf16_t*)w.ws3, (bf16_t*)a.h_routed,
+             (bf16_t*)a.h_shared, (int)d.T, d.D, d.I, d.S, d.E);
+  MOE_LAUNCH((gemm_wstream_bf16<1, NT, TK1>), dim3(g1), dim3(64 * WS_WAVES), WS_LDS, s, nullptr,
+             (const bf16_t*)a.h_routed, (const bf16_t*)a.h_shared, a.row_token, a.offsets,
+             TK1 == kTk128 ? a.tiles_wide : a.tiles_wide2, a.meta, (const bf16_t*)w.w2, nullptr,
+             (const bf16_t*)w.ws2, nullptr, (bf16_t*)a.o_routed, (bf16_t*)a.o_shared, (int)d.T, d.D, d.I, d.S, d.E);
   return hipGetLastError();
 }
 
-// A dense layer of this many tokens or more takes the 256-row tiles: one weight matrix shared by
-// every M-tile, all tiles full, activations that stay in L2, so the larger tile's third fewer bytes
-// per flop through the load path win (4096 tokens, dim 7168, inter 18,432: 2.98 -> 2.77 ms per
-// layer). With routed experts the 128-row tiles stay faster, whatever the experts' sizes.
+// A dense layer of this many tokens or more runs its down projection on 256-row tiles: one weight
+// matrix shared by every M-tile, all tiles full, activations that stay in L2, so the larger tile's
+// third fewer bytes per flop through the load path win (4096 tokens, dim 7168, inter 18,432: down
+// 1.09 -> 0.98 ms). With routed experts the 128-row down projection is the faster one.
 constexpr int64_t kDenseTallRows = 1024;
 
 hipError_t launch_wstream_bf16(const Dims& d, const ExpertPtrs& w, const Act& a, hipStream_t s) {
-  if (d.E == 0 && d.T >= kDenseTallRows) return launch_wstream_nt<false, 256>(d, w, a, s);
+  if (d.E == 0 && d.T >= kDenseTallRows) return launch_wstream_nt<false, kTk256>(d, w, a, s);
   // nontemporal weight loads while the routed experts average fewer rows than one M-tile
-  if (d.R < (int64_t)kWideBM * d.E) return launch_wstream_nt<true, 128>(d, w, a, s);
-  return launch_wstream_nt<false, 128>(d, w, a, s);
+  if (d.R < (int64_t)kWideBM * d.E) return launch_wstream_nt<true, kTk128>(d, w, a, s);
+  return launch_wstream_nt<false, kTk128>(d, w, a, s);
 }
 
 }  // namespace moe
