@@ -53,6 +53,19 @@ def test_ffn_small_all_tokens(name, T):
     say(f"  out {rep}")
 
 
+@pytest.mark.parametrize("T", [128, 129, 192, 193, 256, 257, 384, 385])
+def test_ffn_paired_tile_edges(T):
+    """The bf16 gate/up kernel takes 256-row tiles as one or two 128-row halves: tiles of exactly
+    128 rows (one half), 129 (a second half of one row), 192 / 193 (a second half of 64 / 65 rows,
+    where its multiplied row groups round up from 2 to 4), 256 (two full halves) and a last tile of
+    1 or 129 rows after full ones. Every token checked."""
+    shape = SMALL["dense_wstream_bf16"].with_tokens(T)
+    say(f"[ffn/paired edges] T={T}")
+    tens = inputs.generate_ffn(shape, seed=6, device=DEV)
+    _, out = run_ffn(tens, T)
+    say(f"  out {out_check(shape, to_np(out), oracle_ffn(tens))}")
+
+
 @pytest.mark.parametrize("shape", GROUPED, ids=lambda s: s.name)
 def test_ffn_grouped_order_all_tokens(shape):
     say(f"[ffn/grouped] {shape.name} T={shape.tokens}")

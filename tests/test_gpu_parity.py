@@ -203,6 +203,24 @@ def test_forward_beyond_2gb_activations(name, T):
     say(f"  out {out_check(shape, got, f.out, skip=bad[sample])}")
 
 
+@pytest.mark.parametrize("T", [129, 193, 256, 257])
+def test_paired_tiles_every_expert_all_tokens(T):
+    """Every token takes all 4 experts (top-4 of 4), so each routed expert and the shared expert
+    have exactly T rows: the bf16 gate/up kernel's 256-row tiles as 128-row halves at their edges
+    (a second half of 1 or 65 rows, two full halves, a full pair and a 1-row tile), every token."""
+    shape = S("pair_edges_bf16", tokens=T, dim=256, n_experts=4, n_groups=1, topk_groups=1, topk=4, inter=256,
+              n_shared=1, route_scale=1.0, dtype="bf16")
+    say(f"[forward/paired tiles] T={T}")
+    tens = inputs.generate(shape, seed=13, device=DEV)
+    blk, out = run_block(tens)
+    f = oracle_forward(tens)
+    gidx, gw = gpu_route(blk, shape, T)
+    bad, rep = route_check(shape, f.route, gidx, gw)
+    counts = gpu_dispatch(blk, shape, T)[0]
+    assert (counts == T).all()
+    say(f"  route {rep}\n  out {out_check(shape, to_np(out), f.out, skip=bad)}")
+
+
 @pytest.mark.parametrize("name,T", [("mid_bf16", 1), ("mid_bf16", 17), ("mid_bf16", 64), ("mid_fp8", 3),
                                     ("mid_fp8", 40), ("mid_fp8", 129), ("wstream_fp8", 64),
                                     ("wstream_fp8", 257)])
