@@ -25,8 +25,9 @@
 // (issued in one burst before them, the twelve loads held up the MFMAs: 3% slower). Vector-memory
 // loads complete in issue order; each step issues its weight loads (HBM latency) before its
 // activation loads (L2 hits, needed three steps later), so the wait at step n leaves stage n + 1,
-// slab n + 1 and stage n + 2 in flight (activations first measured 1-2% slower). The step sequence runs on across the block's items without draining: an item's last
-// steps request the next item's first stages. A ragged tile multiplies only its live 32-row groups.
+// slab n + 1 and stage n + 2 in flight (activations first measured 1-2% slower). The step sequence
+// runs on across the block's items without draining: an item's last steps request the next item's
+// first stages. A ragged tile multiplies only its live 32-row groups.
 //
 // Tile kinds. The down projection runs on the 128-row tile list (kTk128; a dense layer of 1024
 // tokens or more on the 256-row list with steps over all 256 rows, kTk256: the same weight slabs,
