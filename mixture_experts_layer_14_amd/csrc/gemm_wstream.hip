@@ -103,7 +103,10 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
   const int items = nr * per_r + (meta[LIST == kWideBM ? 3 : 6] - nr) * per_s;
   // this block's items: xcd * chunk + slot + i * per_xcd for i < mine (an XCD's blocks share a range)
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
-  const int chunk = (items + 7) >> 3;
+  // gate/up: each XCD's range starts at a multiple of per_r items (one tile's column items), so the
+  // blocks that take a round's consecutive items cover whole tiles (16 of them per tile for inter
+  // 2048: half of an XCD's 32 blocks) and share its activation rows
+  const int chunk = MODE == 0 ? (((items + 7) >> 3) + per_r - 1) / per_r * per_r : (items + 7) >> 3;
   const int lim = min(chunk, items - xcd * chunk);
   const int mine = slot < lim ? (lim - slot + per_xcd - 1) / per_xcd : 0;
   if (mine == 0) return;
