@@ -284,7 +284,7 @@ SIDE_WORKLOADS = ["tiny_fp32", "prefill_bf16", "skewed_bf16", "prefill_fp8"]
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
               f"multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     import torch
