@@ -33,22 +33,37 @@ __global__ __launch_bounds__(256) void dispatch_scan(int32_t* __restrict__ blk, 
   __shared__ int off[1025];
   __shared__ int scratch[8];
   const int per = (E + 255) / 256;
+  constexpr int NB = 16;  // token blocks whose counts are loaded together (the loads' latency overlaps)
   // per expert: running base across token blocks (block order = token order)
   for (int j = 0; j < per; ++j) {
     int e = threadIdx.x * per + j;
     if (e >= E) break;
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      int c = blk[(size_t)b * E + e];
-      blk[(size_t)b * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += NB) {
+      int c[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) c[i] = b0 + i < nblk ? blk[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        if (b0 + i < nblk) blk[(size_t)(b0 + i) * E + e] = run;
+        run += c[i];
+      }
     }
     cnt[e] = run;
   }
   __syncthreads();
   publish(cnt, off, E, T, counts, offsets, meta, tiles_s, tiles_w, tiles_w2, scratch);
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
-    for (int b = 0; b < nblk; ++b) blk[(size_t)b * E + e] += off[e];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int o = off[e];
+    for (int b0 = 0; b0 < nblk; b0 += NB) {
+      int c[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) c[i] = b0 + i < nblk ? blk[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if (b0 + i < nblk) blk[(size_t)(b0 + i) * E + e] = c[i] + o;
+    }
+  }
 }
 
 __global__ __launch_bounds__(TB) void dispatch_single(const int32_t* __restrict__ idx, int T, int K, int E,

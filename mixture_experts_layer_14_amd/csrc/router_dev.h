@@ -139,12 +139,13 @@ MOE_DEV void logits_tile(const bf16_t* __restrict__ x, const bf16_t* __restrict_
 //     token's experts (fp64, the sum taken per thread, then per wave in lane order, then over the
 //     waves in order; rounded once to fp32); selection score sb = s + bias
 //   - group score: best + second-best sb of the group (best alone without bias); groups of
-//     2..64 experts (a power of two) sit on consecutive lanes and a butterfly finds them,
+//     2..64 experts (a power of two) sit on consecutive lanes and DPP steps find them,
 //     otherwise one thread per group scans it in LDS
 //   - keep the Gk best groups (ties: lower group); experts of other groups drop to -inf
 //   - choices in descending sb, ties to the lower index: with a block per token every expert
 //     counts the masked scores ranked before it (rank k < K makes it choice k); with a wave per
-//     token, K rounds of wave argmax
+//     token, each lane sorts its own experts once and K rounds take the wave's best head (a DPP
+//     max, then a ballot of the lanes holding it)
 //   - weights: the chosen experts' s over their sum taken in choice order, times route_scale
 //     (softmax scoring: the chosen s times route_scale, not renormalised)
 // ---------------------------------------------------------------------------
@@ -181,6 +182,46 @@ MOE_DEV double token_sum(double v, double* sh) {
   }
 }
 
+// Cross-lane steps inside a wave through DPP: the value of another lane of the same row of 16
+// (quad_perm, the mirrors) or of the row before (row_bcast), read by a VALU move. Lanes of rows
+// outside ROWS keep `old`. Every lane of the wave must be active.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]: lane ^ 1
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]: lane ^ 2
+constexpr int kDppMirror = 0x140;     // lane 15 - i of the row
+constexpr int kDppHalfMirror = 0x141; // lane 7 - i of the half row
+constexpr int kDppBcast15 = 0x142;    // lane 15 of the row before
+constexpr int kDppBcast31 = 0x143;    // lane 31, to rows 2 and 3
+
+template <int CTRL, int ROWS = 0xf>
+MOE_DEV int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS = 0xf>
+MOE_DEV float dpp_f(float old, float v) {
+  return __int_as_float(dpp_i<CTRL, ROWS>(__float_as_int(old), __float_as_int(v)));
+}
+
+// Wave maximum (float) and minimum (int), returned to every lane: the row reduced with quad_perm
+// and the mirrors, the rows joined with the broadcasts in lane 63, then read from there.
+MOE_DEV float wave_max_f(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v, v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v, v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v, v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v, v));
+  v = fmaxf(v, dpp_f<kDppBcast15, 0xa>(v, v));
+  v = fmaxf(v, dpp_f<kDppBcast31, 0xc>(v, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+MOE_DEV int wave_min_i(int v) {
+  v = min(v, dpp_i<kDppXor1>(v, v));
+  v = min(v, dpp_i<kDppXor2>(v, v));
+  v = min(v, dpp_i<kDppHalfMirror>(v, v));
+  v = min(v, dpp_i<kDppMirror>(v, v));
+  v = min(v, dpp_i<kDppBcast15, 0xa>(v, v));
+  v = min(v, dpp_i<kDppBcast31, 0xc>(v, v));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 // -inf for NaN (a group of +inf and -inf scores sums to NaN): ranks below every group score
 MOE_DEV float nan_low(float v) { return __builtin_isnan(v) ? -INFINITY : v; }
 
@@ -188,6 +229,23 @@ MOE_DEV void top2_merge(float& b, float& c, float b2, float c2) {
   const float hi = fmaxf(b, b2), lo = fminf(b, b2);
   c = fmaxf(lo, fmaxf(c, c2));
   b = hi;
+}
+
+// Best and second best (b, c) of each group of gsize consecutive lanes (a power of two, 2..64,
+// groups aligned in the wave); the group's last lane ends with them. Each step joins two disjoint
+// lane sets: lane pairs, quads, halves of a row (mirrors), rows (row 15 broadcast to the odd
+// rows), row pairs (lane 31 to row 3). Lanes of rows a broadcast skips merge with -inf.
+template <int CTRL, int ROWS = 0xf>
+MOE_DEV void top2_step(float& b, float& c) {
+  top2_merge(b, c, dpp_f<CTRL, ROWS>(-INFINITY, b), dpp_f<CTRL, ROWS>(-INFINITY, c));
+}
+MOE_DEV void group_top2(float& b, float& c, int gsize) {
+  top2_step<kDppXor1>(b, c);
+  if (gsize >= 4) top2_step<kDppXor2>(b, c);
+  if (gsize >= 8) top2_step<kDppHalfMirror>(b, c);
+  if (gsize >= 16) top2_step<kDppMirror>(b, c);
+  if (gsize >= 32) top2_step<kDppBcast15, 0xa>(b, c);
+  if (gsize >= 64) top2_step<kDppBcast31, 0xc>(b, c);
 }
 
 // LDS of one selection block: TPB token slots of TT * EPT experts each.
@@ -280,8 +338,8 @@ MOE_DEV void select_block(int bid, const double* __restrict__ zpart, int nsplit,
     }
     if (lanes_path) {
       float b = sbv[j], c = -INFINITY;
-      for (int off = gsize >> 1; off >= 1; off >>= 1) top2_merge(b, c, __shfl_xor(b, off), __shfl_xor(c, off));
-      if (e < E && e % gsize == 0) gsc[e / gsize] = nan_low(bias ? b + c : b);
+      group_top2(b, c, gsize);
+      if (e < E && e % gsize == gsize - 1) gsc[e / gsize] = nan_low(bias ? b + c : b);
     }
   }
   __syncthreads();
@@ -311,30 +369,46 @@ MOE_DEV void select_block(int bid, const double* __restrict__ zpart, int nsplit,
     mv[j] = (e < E && keep[e / gsize]) ? sbv[j] : -INFINITY;
   }
   if constexpr (TT == 64) {
-    // one wave per token: K rounds of wave argmax (ties: lower index)
-    uint32_t taken = 0;
+    // one wave per token. Each lane orders its experts by (masked score descending, index
+    // ascending); experts past E hold -inf and the largest indices, so they come last and, with
+    // K at most the experts of the kept groups, are never taken. Each round takes the wave's
+    // best head: the DPP maximum of the heads, the lanes holding it by ballot (several only on
+    // equal scores: then the lowest index of theirs), and the winning lane drops its head.
+    float hv[EPT];
+    int he[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      hv[j] = mv[j];
+      he[j] = tid + TT * j;
+    }
+    // insertion sort, stable: the indices already ascend, so an equal score never moves up
+#pragma unroll
+    for (int j = 1; j < EPT; ++j)
+#pragma unroll
+      for (int i = j; i > 0; --i) {
+        const bool up = hv[i] > hv[i - 1];
+        const float v0 = hv[i - 1], v1 = hv[i];
+        const int e0 = he[i - 1], e1 = he[i];
+        hv[i - 1] = up ? v1 : v0;
+        hv[i] = up ? v0 : v1;
+        he[i - 1] = up ? e1 : e0;
+        he[i] = up ? e0 : e1;
+      }
     for (int k = 0; k < K; ++k) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+      const float best = wave_max_f(hv[0]);
+      const unsigned long long hit = __ballot(hv[0] == best);
+      const int win = __popcll(hit) == 1 ? __builtin_amdgcn_readlane(he[0], __builtin_ctzll(hit))
+                                         : wave_min_i(hv[0] == best ? he[0] : 0x7fffffff);
+      if (tid == 0) sel[k] = win;
+      if (tid == win % TT) {
 #pragma unroll
-      for (int j = 0; j < EPT; ++j) {
-        const int e = tid + TT * j;
-        if (e < E && !((taken >> j) & 1u) && (mv[j] > bv || (mv[j] == bv && e < bi))) {
-          bv = mv[j];
-          bi = e;
+        for (int j = 0; j + 1 < EPT; ++j) {
+          hv[j] = hv[j + 1];
+          he[j] = he[j + 1];
         }
+        hv[EPT - 1] = -INFINITY;
+        he[EPT - 1] = 0x7fffffff;
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if (tid == 0) sel[k] = bi;
-      if (bi % TT == tid) taken |= 1u << (bi / TT);
     }
   } else {
     // a block per token: each expert counts the masked scores ranked before it

@@ -277,6 +277,54 @@ def test_route_without_bias_uses_group_max():
     route_check(shape, r, np_i32(idx), w.cpu().numpy())
 
 
+def _route_only(shape, tens):
+    cfg = moe.config(shape)
+    T, K = shape.tokens, shape.topk
+    ws = torch.empty(moe.workspace_size(cfg, T), dtype=torch.uint8, device=DEV)
+    idx = torch.empty(T, K, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, K, dtype=torch.float32, device=DEV)
+    moe.route(cfg, tens.w_gate, tens.bias, tens.x, idx, w, ws)
+    torch.cuda.synchronize()
+    return np_i32(idx), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("T", [40, 300])
+def test_route_exact_ties_take_the_lower_index(T):
+    """Experts with bit-identical scores (duplicated router rows and biases) are ordered by index:
+    pairs held by one lane (e, e + 64) and by neighbouring lanes (e, e + 1), in a block per token
+    (40 tokens) and a wave per token (300). Every token must match the oracle exactly."""
+    shape = inputs.WORKLOADS["decode_bf16"].replace(name="ties", tokens=T, dim=256, inter=64)
+    say(f"[route/exact ties] T={T}")
+    tens = inputs.generate(shape, seed=21, device=DEV)
+    wg, b = tens.w_gate, tens.bias
+    wg[64:128] = wg[0:64]          # same lane, next slot
+    b[64:128] = b[0:64]
+    wg[129:192:2] = wg[128:192:2]  # neighbouring lanes, same group
+    b[129:192:2] = b[128:192:2]
+    gi, gw = _route_only(shape, tens)
+    r = O.route(shape, exact(tens.x), exact(wg), bias_np(tens))
+    both = sum(int(np.isin([e, e + 64], r.idx[t]).all()) for t in range(T) for e in range(64))
+    assert both > 0, "no token chose both experts of a tied pair"
+    assert (gi == r.idx).all(), f"{int((gi != r.idx).any(axis=1).sum())} tokens differ"
+    _, rep = route_check(shape, r, gi, gw)
+    say(f"  tokens holding a same-lane tied pair: {both}; {rep}")
+
+
+@pytest.mark.parametrize("T", [40, 300])
+@pytest.mark.parametrize("E,G,Gk,K", [(64, 1, 1, 6), (128, 2, 1, 8), (32, 16, 4, 6), (256, 16, 6, 8)])
+def test_route_group_sizes(T, E, G, Gk, K):
+    """Group scores for every power-of-two group size the lane steps handle (64, 64, 2, 16 experts
+    per group), with a block per token (40 tokens) and a wave per token (300)."""
+    shape = inputs.WORKLOADS["decode_bf16"].replace(name=f"groups_{E}x{G}", tokens=T, dim=256, inter=64,
+                                                    n_experts=E, n_groups=G, topk_groups=Gk, topk=K)
+    say(f"[route/group sizes] T={T} E={E} G={G}")
+    tens = inputs.generate(shape, seed=22, device=DEV)
+    gi, gw = _route_only(shape, tens)
+    r = O.route(shape, exact(tens.x), exact(tens.w_gate), bias_np(tens))
+    _, rep = route_check(shape, r, gi, gw)
+    say(f"  {rep}")
+
+
 @pytest.mark.parametrize("T,D,E,G,Gk,K", [(4000, 7168, 256, 8, 4, 8), (1100, 1152, 72, 8, 4, 6),
                                            (1024, 512, 320, 8, 4, 8)])
 def test_route_large_batch_tiles(T, D, E, G, Gk, K):
