@@ -85,6 +85,16 @@ MOE_DEV void slab_mma(f32x4 acc[NM], const i32x4 a[4], const char* lds, int k0, 
   }
 }
 
+// Workers that take part when `items` equal items go round-robin over at most `workers`: just
+// enough for the same number of rounds, so that every worker's share is that number or one less
+// and the stream ends on all of them together (with every worker busy, the few that hold one more
+// item than the rest finish alone, at a fraction of the bandwidth).
+MOE_DEV int balanced_workers(int items, int workers) {
+  if (items <= 0) return 0;
+  const int rounds = (items + workers - 1) / workers;
+  return (items + rounds - 1) / rounds;
+}
+
 // Both kernels run each wave through a flat sequence of steps (one slab of one item each) with
 // two weight slabs in flight: step n multiplies the slab held in register set n % 2, after storing
 // it to the wave's LDS slab and requesting slab n + 2 into the same registers. The request cursor
@@ -162,8 +172,10 @@ MOE_DEV void gemm1_stream_run(int bid, int nblocks, char (*lds)[2 * SLAB], const
   const int nslab = (D + SK - 1) / SK;
   const int kb = (nslab * wave / G1_WAVES) * SK;
   const int ke = min(D, (nslab * (wave + 1) / G1_WAVES) * SK);
+  // the items of block b: b, b + nblocks, ... over the blocks that take part
+  nblocks = balanced_workers(items, nblocks);
   int item = bid;
-  if (item >= items) return;
+  if (item >= nblocks) return;
   f32x4* red = reinterpret_cast<f32x4*>(lds[wave]);
   auto info_at = [&](int it) { return g1_info(it, tiles, nr, per_r, per_s, w1, w3, ws1, ws3, D, I, E); };
 
@@ -325,9 +337,10 @@ MOE_DEV void gemm2_stream_run(int bid, int nblocks, char (*lds)[SLAB], const bf1
   const int r = lane & 15, q = lane >> 4;
   const int per = D / 16;
   const int items = meta[1] * per * ksplit;
-  const int stride = nblocks * NW;
+  // the items of wave w: w, w + stride, ... over the waves that take part
+  const int stride = balanced_workers(items, nblocks * NW);
   int item = bid * NW + wave;
-  if (item >= items) return;
+  if (item >= stride) return;
   auto info_at = [&](int it) { return g2_info(it, tiles, per, ksplit, w2, ws2, D, I, S, E); };
 
   int l_item = item, l_k0 = 0;
