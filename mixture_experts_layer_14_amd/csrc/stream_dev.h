@@ -85,10 +85,10 @@ MOE_DEV void slab_mma(f32x4 acc[NM], const i32x4 a[4], const char* lds, int k0, 
   }
 }
 
-// Workers that take part when `items` equal items go round-robin over at most `workers`: just
-// enough for the same number of rounds, so that every worker's share is that number or one less
-// and the stream ends on all of them together (with every worker busy, the few that hold one more
-// item than the rest finish alone, at a fraction of the bandwidth).
+// How many of `workers` take `items` equal items round-robin: the fewest that still need only
+// ceil(items / workers) rounds. Every worker's share is then that number of items or one less, so
+// all of them finish together; with every worker busy, the few holding one item more than the
+// rest would stream alone at the end, at a fraction of the bandwidth.
 MOE_DEV int balanced_workers(int items, int workers) {
   if (items <= 0) return 0;
   const int rounds = (items + workers - 1) / workers;
