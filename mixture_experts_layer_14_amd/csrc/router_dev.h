@@ -136,8 +136,8 @@ MOE_DEV void logits_tile(const bf16_t* __restrict__ x, const bf16_t* __restrict_
 // otherwise); thread i of a token owns experts i, i + TT, ...
 //   - z: the token's fp64 partial logits summed in slice order, rounded once to fp32
 //   - s = sigmoid(z), or with softmax scoring s = exp(z - max z) / sum exp(z - max z) over the
-//     token's experts (fp64, the sum taken per thread, then per wave in lane order, then over the
-//     waves in order; rounded once to fp32); selection score sb = s + bias
+//     token's experts (fp64, the sum taken per thread, then over the wave in a fixed tree of DPP
+//     steps, then over the waves in order; rounded once to fp32); selection score sb = s + bias
 //   - group score: best + second-best sb of the group (best alone without bias); groups of
 //     2..64 experts (a power of two) sit on consecutive lanes and DPP steps find them,
 //     otherwise one thread per group scans it in LDS
@@ -150,37 +150,6 @@ MOE_DEV void logits_tile(const bf16_t* __restrict__ x, const bf16_t* __restrict_
 //     (softmax scoring: the chosen s times route_scale, not renormalised)
 // ---------------------------------------------------------------------------
 constexpr int kMaxE = 1024, kMaxG = 64, kMaxK = 16;
-
-// Reductions over the TT threads of one token: a wave (TT = 64) or the whole block (TT = 256,
-// the wave results combined in wave order through sh[4]).
-template <int TT>
-MOE_DEV float token_max(float v, double* sh) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  if constexpr (TT == 64) {
-    return v;
-  } else {
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-    __syncthreads();
-    const float r = fmaxf(fmaxf((float)sh[0], (float)sh[1]), fmaxf((float)sh[2], (float)sh[3]));
-    __syncthreads();
-    return r;
-  }
-}
-template <int TT>
-MOE_DEV double token_sum(double v, double* sh) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  if constexpr (TT == 64) {
-    return v;
-  } else {
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-    __syncthreads();
-    const double r = ((sh[0] + sh[1]) + sh[2]) + sh[3];
-    __syncthreads();
-    return r;
-  }
-}
 
 // Cross-lane steps inside a wave through DPP: the value of another lane of the same row of 16
 // (quad_perm, the mirrors) or of the row before (row_bcast), read by a VALU move. Lanes of rows
@@ -212,6 +181,29 @@ MOE_DEV float wave_max_f(float v) {
   v = fmaxf(v, dpp_f<kDppBcast31, 0xc>(v, v));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+// Wave sum (fp64), returned to every lane: the same steps as the maximum, each adding the sums of
+// two disjoint lane sets, so the additions form one fixed tree (lane pairs, quads, half rows, rows,
+// row pairs) and the total does not depend on timing. Rows a broadcast skips add zero; only lane
+// 63's value is read.
+template <int CTRL, int ROWS = 0xf>
+MOE_DEV double dpp_d(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = dpp_i<CTRL, ROWS>(0, (int)(b & 0xffffffffll));
+  const int hi = dpp_i<CTRL, ROWS>(0, (int)(b >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+MOE_DEV double wave_sum_d(double v) {
+  v = v + dpp_d<kDppXor1>(v);
+  v = v + dpp_d<kDppXor2>(v);
+  v = v + dpp_d<kDppHalfMirror>(v);
+  v = v + dpp_d<kDppMirror>(v);
+  v = v + dpp_d<kDppBcast15, 0xa>(v);
+  v = v + dpp_d<kDppBcast31, 0xc>(v);
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), 63);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
 MOE_DEV int wave_min_i(int v) {
   v = min(v, dpp_i<kDppXor1>(v, v));
   v = min(v, dpp_i<kDppXor2>(v, v));
@@ -220,6 +212,35 @@ MOE_DEV int wave_min_i(int v) {
   v = min(v, dpp_i<kDppBcast15, 0xa>(v, v));
   v = min(v, dpp_i<kDppBcast31, 0xc>(v, v));
   return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Reductions over the TT threads of one token: a wave (TT = 64) or the whole block (TT = 256,
+// the wave results combined in wave order through sh[4]).
+template <int TT>
+MOE_DEV float token_max(float v, double* sh) {
+  v = wave_max_f(v);
+  if constexpr (TT == 64) {
+    return v;
+  } else {
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const float r = fmaxf(fmaxf((float)sh[0], (float)sh[1]), fmaxf((float)sh[2], (float)sh[3]));
+    __syncthreads();
+    return r;
+  }
+}
+template <int TT>
+MOE_DEV double token_sum(double v, double* sh) {
+  v = wave_sum_d(v);
+  if constexpr (TT == 64) {
+    return v;
+  } else {
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const double r = ((sh[0] + sh[1]) + sh[2]) + sh[3];
+    __syncthreads();
+    return r;
+  }
 }
 
 // -inf for NaN (a group of +inf and -inf scores sums to NaN): ranks below every group score
