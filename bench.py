@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -106,16 +107,31 @@ def kernel_key(name):
     return f"{base.strip()}<{rest.split(',')[0].split('>')[0].strip()}>"
 
 
-def source_hash(kernel):
-    """Hash of the source file that defines `kernel` plus the headers: the counters of a kernel
-    stay valid while none of these change."""
+_INCLUDE = re.compile(r'^\s*#\s*include\s+"([^"]+)"', re.M)
+
+
+def source_files(kernel):
+    """The source file that defines `kernel` and every header of the library it includes,
+    directly or through other headers."""
     base = kernel_base(kernel)
-    files = [f for f in sorted(os.listdir(CSRC)) if f.endswith(".h")]
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith(".hip") and f"void {base}(" in open(os.path.join(CSRC, f)).read():
-            files.append(f)
+    todo = [f for f in sorted(os.listdir(CSRC))
+            if f.endswith(".hip") and f"void {base}(" in open(os.path.join(CSRC, f)).read()]
+    seen = set()
+    while todo:
+        f = todo.pop()
+        if f in seen or not os.path.exists(os.path.join(CSRC, f)):
+            continue
+        seen.add(f)
+        todo.extend(_INCLUDE.findall(open(os.path.join(CSRC, f)).read()))
+    return sorted(seen)
+
+
+def source_hash(kernel):
+    """Hash of the files `kernel` is compiled from (source_files): the counters of a kernel stay
+    valid while none of these change."""
     h = hashlib.sha256()
-    for f in files:
+    for f in source_files(kernel):
+        h.update(f.encode())
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -37,6 +37,18 @@ def test_source_hash_covers_the_defining_file():
     assert h != bench.source_hash("combine<true>")  # different defining file
 
 
+def test_source_files_follow_the_includes():
+    """A kernel's counters depend on its own file and the headers it includes, directly or not."""
+    ws = bench.source_files("gemm_wstream_bf16<0>")
+    assert "gemm_wstream.hip" in ws and "wstream.h" in ws and "kernels.h" in ws
+    assert "router_dev.h" not in ws and "router.hip" not in ws
+    sel = bench.source_files("router_select<4>")
+    assert "router.hip" in sel and "router_dev.h" in sel
+    fused = bench.source_files("decode_fused")
+    for h in ("router_dev.h", "dispatch_dev.h", "stream_dev.h", "combine_dev.h"):
+        assert h in fused
+
+
 def test_committed_traffic_entries_are_well_formed():
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     recs = json.load(open(path))
