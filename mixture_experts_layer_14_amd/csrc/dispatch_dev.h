@@ -33,29 +33,6 @@ __device__ __forceinline__ void build_bits(unsigned long long* bits, const int32
   __syncthreads();
 }
 
-// Exclusive scan of v over the block (blockDim.x threads, at most 8 waves); returns the block total
-// in *total.
-MOE_DEV int block_exclusive_scan(int v, int* scratch /*[8]*/, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  if (lane == 63) scratch[wave] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-    int sw = scratch[w];
-    if (w < wave) before += sw;
-    all += sw;
-  }
-  __syncthreads();
-  *total = all;
-  return before + incl - v;
-}
-
 // Tiles of one list: routed experts ascending (M-tiles of `bm` dispatch rows), then the
 // shared expert (index E) over all T tokens.
 MOE_DEV void write_tiles(const int* cnt, const int* off, int E, int T, int bm, Tile* tiles, int32_t* meta_routed,

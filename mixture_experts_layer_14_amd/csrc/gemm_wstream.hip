@@ -101,15 +101,86 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
   const int per_s = MODE == 0 ? S / HN : D / HN;
   const int nr = meta[LIST == kWideBM ? 2 : 5];
   const int items = nr * per_r + (meta[LIST == kWideBM ? 3 : 6] - nr) * per_s;
-  // this block's items: xcd * chunk + slot + i * per_xcd for i < mine (an XCD's blocks share a range)
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
-  // gate/up: each XCD's range starts at a multiple of per_r items (one tile's column items), so the
-  // blocks that take a round's consecutive items cover whole tiles (16 of them per tile for inter
-  // 2048: half of an XCD's 32 blocks) and share its activation rows
-  const int chunk = MODE == 0 ? (((items + 7) >> 3) + per_r - 1) / per_r * per_r : (items + 7) >> 3;
-  const int lim = min(chunk, items - xcd * chunk);
-  const int mine = slot < lim ? (lim - slot + per_xcd - 1) / per_xcd : 0;
+  // Gate/up (paired tiles): the blocks form runs of 16 (two per XCD), each run a contiguous range of
+  // whole tiles holding an equal share of the launch's work. A tile's cost is its column items
+  // times an item's measured time by kind (fitted to the blocks' end times at 4096 tokens, uniform
+  // and skewed routing): a tile of at most 64 rows 12, of at most 128 rows 15, a paired tile (two
+  // half-steps per k-step) 20, a tile of a routed expert with more than one (its weight tiles are
+  // read by several blocks at once, mostly from L2) 17, a shared-expert tile 20. The run's 16
+  // blocks take its items in rounds of 16 consecutive ones
+  // (one tile's column items when a tile has 16), so the items that run together are the ones the
+  // plain order runs together, and a block's place in the round moves by one each round, so no
+  // block always takes the same M-tile of an expert. Dealt by count instead, the blocks that drew
+  // more paired tiles finished up to a quarter of the launch after the rest.
+  // Otherwise: this block's items are xcd * chunk + slot + i * per_xcd for i < mine (an XCD's
+  // blocks share a range); gate/up ranges start at a multiple of per_r items (one tile's column
+  // items), so the blocks that take a round's consecutive items share its activation rows.
+  constexpr int kRunBlocks = 16;
+  const int ntiles = meta[LIST == kWideBM ? 3 : 6];
+  const bool runs = MODE == 0 && TK == kTkPair && per_xcd % kRunBlocks == 0;
+  int run_lo = 0, run_hi = 0, chunk = 0, mine = 0;
+  if (runs) {
+    constexpr int kCostSmall = 12, kCostSingle = 15, kCostPaired = 20, kCostMulti = 17, kCostShared = 20;
+    int* red = reinterpret_cast<int*>(lds);  // scan scratch [8], then the run bounds [2]; no load has
+                                             // written the LDS yet
+    const int nthr = 64 * WS_WAVES;
+    const int per_t = (ntiles + nthr - 1) / nthr;
+    const int t0 = min(ntiles, (int)threadIdx.x * per_t), t1 = min(ntiles, t0 + per_t);
+    auto tile_cost = [&](int t) __attribute__((always_inline)) {
+      if (t >= nr) return kCostShared * per_s;
+      const Tile tl = tiles[t];
+      const int c = offsets[tl.expert + 1] - offsets[tl.expert] > LIST ? kCostMulti
+                    : tl.nrows > 128                                   ? kCostPaired
+                    : tl.nrows > 64                                    ? kCostSingle
+                                                                       : kCostSmall;
+      return c * per_r;
+    };
+    auto tile_item = [&](int t) __attribute__((always_inline)) {
+      return t < nr ? t * per_r : nr * per_r + (t - nr) * per_s;
+    };
+    int mine_cost = 0;
+    for (int t = t0; t < t1; ++t) mine_cost += tile_cost(t);
+    int total = 0;
+    const int before = block_exclusive_scan(mine_cost, red, &total);
+    const int nruns = (int)(gridDim.x / kRunBlocks), run = xcd * (per_xcd / kRunBlocks) + slot / kRunBlocks;
+    // run bounds: the tile boundary nearest to total * r / nruns, for r = run and run + 1
+    if (threadIdx.x == 0) {
+      red[8] = run == 0 ? 0 : -1;
+      red[9] = run + 1 == nruns ? items : -1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int r = run + b;
+      if (r == 0 || r == nruns) continue;
+      const int64_t target = (int64_t)total * r / nruns;
+      int acc = before;
+      for (int t = t0; t < t1; ++t) {
+        const int c = tile_cost(t);
+        if (acc <= target && target < acc + c) red[8 + b] = tile_item(2 * (target - acc) < c ? t : t + 1);
+        acc += c;
+      }
+    }
+    __syncthreads();
+    run_lo = red[8];
+    run_hi = red[9];
+    __syncthreads();  // every bound is read before the first load writes the LDS
+    // with no tiles there is no work (and no bound was found)
+    if (total > 0 && run_lo >= 0 && run_hi > run_lo) {
+      const int q = (run_hi - run_lo) / kRunBlocks, rest = (run_hi - run_lo) % kRunBlocks;
+      mine = q + ((((slot % kRunBlocks) + q) % kRunBlocks) < rest ? 1 : 0);
+    }
+  } else {
+    chunk = MODE == 0 ? (((items + 7) >> 3) + per_r - 1) / per_r * per_r : (items + 7) >> 3;
+    const int lim = min(chunk, items - xcd * chunk);
+    mine = slot < lim ? (lim - slot + per_xcd - 1) / per_xcd : 0;
+  }
   if (mine == 0) return;
+  // the list index of this block's i-th item (i < mine)
+  auto item_index = [&](int i) __attribute__((always_inline)) {
+    return runs ? run_lo + kRunBlocks * i + (((slot % kRunBlocks) + i) % kRunBlocks) : xcd * chunk + slot + i * per_xcd;
+  };
   const int nk = (MODE == 0 ? D : I) / WS_BK;  // steps per item (the shared expert has S == I)
 
   auto item_of = [&](int i) __attribute__((always_inline)) {
@@ -117,7 +188,7 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
     d.live = i < mine;
     d.row0 = 0, d.nrows = 0, d.nt = 0, d.expert = 0, d.rot = 0, d.sh = false, d.solo = false;
     if (d.live) {
-      const WideItem it = wide_item<LIST>(xcd * chunk + slot + i * per_xcd, tiles, nr, offsets, T, E, per_r, per_s);
+      const WideItem it = wide_item<LIST>(item_index(i), tiles, nr, offsets, T, E, per_r, per_s);
       d.row0 = it.tl.row0;
       d.nrows = it.tl.nrows;
       d.nt = it.nt;

@@ -152,6 +152,29 @@ struct WideItem {
   bool shared;
 };
 
+// Exclusive scan of v over the block (blockDim.x threads, at most 8 waves); returns the block total
+// in *total. scratch: 8 ints of LDS.
+MOE_DEV int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    int sw = scratch[w];
+    if (w < wave) before += sw;
+    all += sw;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
 // item -> (tile, n-tile): routed items first (per_r n-tiles per expert), then the shared
 // expert's (per_s). Within an expert the M-tiles go in round(mt / kGroupM) groups of nearly equal
 // size (the first mt % groups one larger); a group's items run n-tile by n-tile, its M-tiles
