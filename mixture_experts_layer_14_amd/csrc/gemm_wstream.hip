@@ -107,12 +107,12 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
   // times an item's measured time by kind (fitted to the blocks' end times at 4096 tokens, uniform
   // and skewed routing): a tile of at most 64 rows 12, of at most 128 rows 15, a paired tile (two
   // half-steps per k-step) 20, a tile of a routed expert with more than one (its weight tiles are
-  // read by several blocks at once, mostly from L2) 17, a shared-expert tile 20. The run's 16
-  // blocks take its items in rounds of 16 consecutive ones
-  // (one tile's column items when a tile has 16), so the items that run together are the ones the
-  // plain order runs together, and a block's place in the round moves by one each round, so no
-  // block always takes the same M-tile of an expert. Dealt by count instead, the blocks that drew
-  // more paired tiles finished up to a quarter of the launch after the rest.
+  // read by several blocks at once, mostly from L2) 17, a shared-expert tile 20. A run's 16 blocks
+  // take its items in rounds of 16 consecutive ones (one tile's column items when a tile has 16), so
+  // the items that run together are the ones the plain order runs together; a block's place in the
+  // round moves by one each round, so no block always takes the same M-tile of an expert. Dealt by
+  // count instead, the blocks that drew more paired tiles finished up to a quarter of the launch
+  // after the rest.
   // Otherwise: this block's items are xcd * chunk + slot + i * per_xcd for i < mine (an XCD's
   // blocks share a range); gate/up ranges start at a multiple of per_r items (one tile's column
   // items), so the blocks that take a round's consecutive items share its activation rows.
