@@ -116,17 +116,12 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
   // Otherwise: this block's items are xcd * chunk + slot + i * per_xcd for i < mine (an XCD's
   // blocks share a range); gate/up ranges start at a multiple of per_r items (one tile's column
   // items), so the blocks that take a round's consecutive items share its activation rows.
-  constexpr int kRunBlocks = 16;
   const int ntiles = meta[LIST == kWideBM ? 3 : 6];
   const bool runs = MODE == 0 && TK == kTkPair && per_xcd % kRunBlocks == 0;
+  const int pos = slot % kRunBlocks;
   int run_lo = 0, run_hi = 0, chunk = 0, mine = 0;
   if (runs) {
     constexpr int kCostSmall = 12, kCostSingle = 15, kCostPaired = 20, kCostMulti = 17, kCostShared = 20;
-    int* red = reinterpret_cast<int*>(lds);  // scan scratch [8], then the run bounds [2]; no load has
-                                             // written the LDS yet
-    const int nthr = 64 * WS_WAVES;
-    const int per_t = (ntiles + nthr - 1) / nthr;
-    const int t0 = min(ntiles, (int)threadIdx.x * per_t), t1 = min(ntiles, t0 + per_t);
     auto tile_cost = [&](int t) __attribute__((always_inline)) {
       if (t >= nr) return kCostShared * per_s;
       const Tile tl = tiles[t];
@@ -139,38 +134,11 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
     auto tile_item = [&](int t) __attribute__((always_inline)) {
       return t < nr ? t * per_r : nr * per_r + (t - nr) * per_s;
     };
-    int mine_cost = 0;
-    for (int t = t0; t < t1; ++t) mine_cost += tile_cost(t);
-    int total = 0;
-    const int before = block_exclusive_scan(mine_cost, red, &total);
-    const int nruns = (int)(gridDim.x / kRunBlocks), run = xcd * (per_xcd / kRunBlocks) + slot / kRunBlocks;
-    // run bounds: the tile boundary nearest to total * r / nruns, for r = run and run + 1
-    if (threadIdx.x == 0) {
-      red[8] = run == 0 ? 0 : -1;
-      red[9] = run + 1 == nruns ? items : -1;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int r = run + b;
-      if (r == 0 || r == nruns) continue;
-      const int64_t target = (int64_t)total * r / nruns;
-      int acc = before;
-      for (int t = t0; t < t1; ++t) {
-        const int c = tile_cost(t);
-        if (acc <= target && target < acc + c) red[8 + b] = tile_item(2 * (target - acc) < c ? t : t + 1);
-        acc += c;
-      }
-    }
-    __syncthreads();
-    run_lo = red[8];
-    run_hi = red[9];
-    __syncthreads();  // every bound is read before the first load writes the LDS
-    // with no tiles there is no work (and no bound was found)
-    if (total > 0 && run_lo >= 0 && run_hi > run_lo) {
-      const int q = (run_hi - run_lo) / kRunBlocks, rest = (run_hi - run_lo) % kRunBlocks;
-      mine = q + ((((slot % kRunBlocks) + q) % kRunBlocks) < rest ? 1 : 0);
-    }
+    const int run = xcd * (per_xcd / kRunBlocks) + slot / kRunBlocks;
+    // the LDS is free until the prologue's loads
+    if (ws_run_bounds(ntiles, items, run, (int)gridDim.x / kRunBlocks, tile_cost, tile_item,
+                      reinterpret_cast<int*>(lds), run_lo, run_hi))
+      mine = ws_run_count(run_lo, run_hi, pos);
   } else {
     chunk = MODE == 0 ? (((items + 7) >> 3) + per_r - 1) / per_r * per_r : (items + 7) >> 3;
     const int lim = min(chunk, items - xcd * chunk);
@@ -179,7 +147,7 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
   if (mine == 0) return;
   // the list index of this block's i-th item (i < mine)
   auto item_index = [&](int i) __attribute__((always_inline)) {
-    return runs ? run_lo + kRunBlocks * i + (((slot % kRunBlocks) + i) % kRunBlocks) : xcd * chunk + slot + i * per_xcd;
+    return runs ? ws_run_item(run_lo, pos, i) : xcd * chunk + slot + i * per_xcd;
   };
   const int nk = (MODE == 0 ? D : I) / WS_BK;  // steps per item (the shared expert has S == I)
 
