@@ -117,7 +117,9 @@ __global__ __launch_bounds__(64 * WS_WAVES) void gemm_wstream_bf16(
   // blocks share a range); gate/up ranges start at a multiple of per_r items (one tile's column
   // items), so the blocks that take a round's consecutive items share its activation rows.
   const int ntiles = meta[LIST == kWideBM ? 3 : 6];
-  const bool runs = MODE == 0 && TK == kTkPair && per_xcd % kRunBlocks == 0;
+  // (only with at least four tiles per run: a launch of few tiles would otherwise sit on few blocks)
+  const bool runs = MODE == 0 && TK == kTkPair && per_xcd % kRunBlocks == 0 &&
+                    ntiles >= 4 * ((int)gridDim.x / kRunBlocks);
   const int pos = slot % kRunBlocks;
   int run_lo = 0, run_hi = 0, chunk = 0, mine = 0;
   if (runs) {
