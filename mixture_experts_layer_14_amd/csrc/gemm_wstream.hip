@@ -38,6 +38,10 @@
 // activation ring keeps its four 16 KB stages; a tile of at most 128 rows runs as kTk128 does.
 // The per-expert tile height thus follows the expert's row count.
 //
+// Items to blocks. Each XCD's blocks take a contiguous range of the item list. Gate/up launches of
+// enough tiles split it into runs of 16 blocks with equal shares of measured cost, a run's blocks
+// taking its items in lockstep rounds of 16 (see the kernel); the others deal items by count.
+//
 // Steps come in groups of four (the activation stages rotate with the group), so an item's steps
 // (dim / 64 or inter / 64) must be a multiple of four; the epilogue and the accumulator reset run
 // between items, outside the unrolled group. Every wait above is an explicit count: all loads of
